@@ -1,0 +1,214 @@
+"""Python binding of libfa.so, the gfx950 exact IO-aware attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/fa.h.  PyTorch supplies device
+memory and the current stream; tensors are passed as raw device pointers.
+The functions keep the C names (fa_fwd, fa_bwd, ...), take torch tensors of
+layout [B, H, N, d] and raise FAError when the library returns a non-zero
+status.  There is no fallback: if libfa.so is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_BF16, FA_F32 = 0, 1
+WALK_FWD, WALK_DKDV, WALK_DQ = 0, 1, 2
+CELL = 128
+
+EXPORTS = ("fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv",
+           "fa_bwd_dq", "fa_debug_visits", "fa_status_str")
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_str(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so (built by __graft_entry__.build()).  torch is imported first
+    so the library binds to the HIP runtime torch already loaded."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libfa.so not found at {path}; build it with __graft_entry__.build()")
+    try:
+        import torch  # noqa: F401  (HIP runtime first)
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(path)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "fa_fwd": [P, P, P, P, P, I, I, I, I, F, I, P, P, I, P],
+        "fa_bwd_workspace_bytes": [I, I, I, I, I],
+        "fa_bwd": [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, P, S, P],
+        "fa_bwd_preprocess": [P, P, P, I, I, I, I, I, P],
+        "fa_bwd_dkdv": [P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, P],
+        "fa_bwd_dq": [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, P],
+        "fa_debug_visits": [I, I, I, I, I, I, P, P, I, P, P],
+        "fa_status_str": [I],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_str(status: int) -> str:
+    return load_library().fa_status_str(int(status)).decode()
+
+
+# ---------------------------------------------------------------- marshalling helpers
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _shape(t):
+    if t.dim() != 4:
+        raise ValueError("expected a [B, H, N, d] tensor")
+    return tuple(int(x) for x in t.shape)
+
+
+def _check_like(ref, *ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+        if t.device != ref.device:
+            raise ValueError("all tensors must be on the same device")
+
+
+def _call(name, *args):
+    st = getattr(load_library(), name)(*args)
+    if st != 0:
+        raise FAError(st, name)
+
+
+def _mask_args(block_mask, kv_len):
+    return _ptr(block_mask), _ptr(kv_len)
+
+
+def _scale(scale, d):
+    return float(1.0 / math.sqrt(d) if scale is None else scale)
+
+
+# ---------------------------------------------------------------- entry points
+
+def fa_fwd(q, k, v, o=None, lse=None, *, scale=None, causal=False, block_mask=None, kv_len=None,
+           stream=None):
+    """O, lse = attention forward.  q, k, v: [B,H,N,d] bf16 or float32 on the GPU;
+    block_mask: uint8 [T,T] (T = ceil(N/128)) or None; kv_len: int32 [B] or None."""
+    import torch
+    B, H, N, d = _shape(q)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_like(q, q, k, v, o, lse, block_mask, kv_len)
+    mb, kl = _mask_args(block_mask, kv_len)
+    _call("fa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _scale(scale, d),
+          int(bool(causal)), mb, kl, _dtype_code(q), _stream(stream))
+    return o, lse
+
+
+def fa_bwd_workspace_bytes(B, H, N, d, dtype=FA_BF16) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, H, N, d, dtype))
+
+
+def fa_bwd(q, k, v, o, dO, lse, dq=None, dk=None, dv=None, *, scale=None, causal=False, block_mask=None,
+           kv_len=None, workspace=None, stream=None):
+    """dQ, dK, dV for the loss gradient dO, from the forward's O and lse."""
+    import torch
+    B, H, N, d = _shape(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = fa_bwd_workspace_bytes(B, H, N, d, _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_like(q, q, k, v, o, dO, lse, dq, dk, dv, workspace, block_mask, kv_len)
+    mb, kl = _mask_args(block_mask, kv_len)
+    _call("fa_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+          B, H, N, d, _scale(scale, d), int(bool(causal)), mb, kl, _dtype_code(q), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(stream))
+    return dq, dk, dv
+
+
+def fa_bwd_preprocess(o, dO, delta=None, *, stream=None):
+    import torch
+    B, H, N, d = _shape(o)
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=o.device)
+    _check_like(o, o, dO, delta)
+    _call("fa_bwd_preprocess", _ptr(o), _ptr(dO), _ptr(delta), B, H, N, d, _dtype_code(o), _stream(stream))
+    return delta
+
+
+def fa_bwd_dkdv(q, k, v, dO, lse, delta, dk=None, dv=None, *, scale=None, causal=False, block_mask=None,
+                kv_len=None, stream=None):
+    import torch
+    B, H, N, d = _shape(q)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_like(q, q, k, v, dO, lse, delta, dk, dv, block_mask, kv_len)
+    mb, kl = _mask_args(block_mask, kv_len)
+    _call("fa_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
+          B, H, N, d, _scale(scale, d), int(bool(causal)), mb, kl, _dtype_code(q), _stream(stream))
+    return dk, dv
+
+
+def fa_bwd_dq(q, k, v, dO, lse, delta, dq=None, *, scale=None, causal=False, block_mask=None, kv_len=None,
+              stream=None):
+    import torch
+    B, H, N, d = _shape(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    _check_like(q, q, k, v, dO, lse, delta, dq, block_mask, kv_len)
+    mb, kl = _mask_args(block_mask, kv_len)
+    _call("fa_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(dq),
+          B, H, N, d, _scale(scale, d), int(bool(causal)), mb, kl, _dtype_code(q), _stream(stream))
+    return dq
+
+
+def fa_debug_visits(which, B, H, N, d, *, causal=False, block_mask=None, kv_len=None, dtype=FA_BF16,
+                    device="cuda", stream=None):
+    """Visit counters [B, T, T] (uint32 stored in int32) of the forward (0),
+    dK/dV (1) or dQ (2) tile walk."""
+    import torch
+    T = -(-N // CELL)
+    counts = torch.zeros((B, T, T), dtype=torch.int32, device=device)
+    mb, kl = _mask_args(block_mask, kv_len)
+    _call("fa_debug_visits", int(which), B, H, N, d, int(bool(causal)), mb, kl, int(dtype), _ptr(counts),
+          _stream(stream))
+    return counts

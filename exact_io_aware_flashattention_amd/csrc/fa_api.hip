@@ -1,0 +1,235 @@
+// C ABI of libfa.so: argument checks, then stream-ordered kernel launches.
+// Every check runs before any HIP call, so a rejected call touches neither
+// the device nor the stream.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_kernels.hpp"
+
+namespace {
+
+constexpr int kCell = 128;
+constexpr int kMaxCells = 2048;
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+struct Shape {
+  int B, H, N, d, dtype;
+};
+
+// Size and type checks shared by every entry point.  Sets *empty when there
+// is nothing to compute.
+int check_shape(const Shape& s, const uint8_t* block_mask, bool* empty) {
+  if (s.dtype != FA_BF16 && s.dtype != FA_F32) return FA_ERR_DTYPE;
+  if (s.B < 0 || s.H < 0 || s.N < 0) return FA_ERR_SHAPE;
+  if (s.d != 64 && s.d != 128) return FA_ERR_SHAPE;
+  *empty = (s.B == 0 || s.H == 0 || s.N == 0);
+  if (*empty) return FA_OK;
+  const long long T = (s.N + kCell - 1) / kCell;
+  if (block_mask && T > kMaxCells) return FA_ERR_SHAPE;
+  // work-group counts and row indices stay within int
+  if (T * s.H * s.B > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if ((long long)s.B * s.H * s.N > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if ((long long)s.N * s.d > 0x7fffffffLL) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_scale(float scale) { return (isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_ARG; }
+
+int check_tensors(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (!p) return FA_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+int check_rowstats(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (!p) return FA_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned(p, 4)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+int check_masks(const uint8_t* block_mask, const int32_t* kv_len) {
+  (void)block_mask;
+  if (kv_len && !aligned(kv_len, 4)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+fa::AttnArgs make_args(const Shape& s, float scale, int causal, const uint8_t* block_mask,
+                       const int32_t* kv_len) {
+  fa::AttnArgs a{};
+  a.B = s.B;
+  a.H = s.H;
+  a.N = s.N;
+  a.scale = scale;
+  a.c = scale * 1.4426950408889634f;
+  a.causal = causal ? 1 : 0;
+  a.mask = block_mask;
+  a.kv_len = kv_len;
+  return a;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+#define FA_TRY(expr)            \
+  do {                          \
+    const int _st = (expr);     \
+    if (_st != FA_OK) return _st; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: unsupported or inconsistent sizes";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype must be FA_BF16 or FA_F32";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not suitably aligned";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: a HIP launch failed";
+    case FA_ERR_ARG: return "FA_ERR_ARG: invalid scale or selector";
+    default: return "unknown fa status";
+  }
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
+  (void)d;
+  (void)dtype;
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  const size_t bytes = (size_t)B * H * N * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, const uint8_t* block_mask, const int32_t* kv_len, int dtype,
+           void* stream) {
+  const Shape s{B, H, N, d, dtype};
+  bool empty = false;
+  FA_TRY(check_shape(s, block_mask, &empty));
+  if (empty) return FA_OK;
+  FA_TRY(check_tensors({q, k, v, o}));
+  FA_TRY(check_rowstats({lse}));
+  FA_TRY(check_masks(block_mask, kv_len));
+  FA_TRY(check_scale(scale));
+  fa::AttnArgs a = make_args(s, scale, causal, block_mask, kv_len);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out0 = o;
+  a.lse = lse;
+  return hip_status(fa::launch_fwd(a, dtype, d, false, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H, int N, int d, int dtype,
+                      void* stream) {
+  const Shape s{B, H, N, d, dtype};
+  bool empty = false;
+  FA_TRY(check_shape(s, nullptr, &empty));
+  if (empty) return FA_OK;
+  FA_TRY(check_tensors({o, dO}));
+  FA_TRY(check_rowstats({delta}));
+  fa::AttnArgs a = make_args(s, 1.f, 0, nullptr, nullptr);
+  a.o = o;
+  a.dO = dO;
+  a.delta = delta;
+  return hip_status(fa::launch_bwd_pre(a, dtype, d, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                const float* delta, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* stream) {
+  const Shape s{B, H, N, d, dtype};
+  bool empty = false;
+  FA_TRY(check_shape(s, block_mask, &empty));
+  if (empty) return FA_OK;
+  FA_TRY(check_tensors({q, k, v, dO, dk, dv}));
+  FA_TRY(check_rowstats({lse, delta}));
+  FA_TRY(check_masks(block_mask, kv_len));
+  FA_TRY(check_scale(scale));
+  fa::AttnArgs a = make_args(s, scale, causal, block_mask, kv_len);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dO = dO;
+  a.lse = const_cast<float*>(lse);
+  a.delta = const_cast<float*>(delta);
+  a.out0 = dk;
+  a.out1 = dv;
+  return hip_status(fa::launch_bwd_dkdv(a, dtype, d, false, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+              const float* delta, void* dq, int B, int H, int N, int d, float scale, int causal,
+              const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* stream) {
+  const Shape s{B, H, N, d, dtype};
+  bool empty = false;
+  FA_TRY(check_shape(s, block_mask, &empty));
+  if (empty) return FA_OK;
+  FA_TRY(check_tensors({q, k, v, dO, dq}));
+  FA_TRY(check_rowstats({lse, delta}));
+  FA_TRY(check_masks(block_mask, kv_len));
+  FA_TRY(check_scale(scale));
+  fa::AttnArgs a = make_args(s, scale, causal, block_mask, kv_len);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dO = dO;
+  a.lse = const_cast<float*>(lse);
+  a.delta = const_cast<float*>(delta);
+  a.out0 = dq;
+  return hip_status(fa::launch_bwd_dq(a, dtype, d, false, static_cast<hipStream_t>(stream)));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+           void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+           const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  const Shape s{B, H, N, d, dtype};
+  bool empty = false;
+  FA_TRY(check_shape(s, block_mask, &empty));
+  if (empty) return FA_OK;
+  FA_TRY(check_tensors({q, k, v, o, dO, dq, dk, dv}));
+  FA_TRY(check_rowstats({lse}));
+  FA_TRY(check_masks(block_mask, kv_len));
+  FA_TRY(check_scale(scale));
+  if (!workspace) return FA_ERR_NULL;
+  if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+  if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
+  float* delta = static_cast<float*>(workspace);
+  FA_TRY(fa_bwd_preprocess(o, dO, delta, B, H, N, d, dtype, stream));
+  FA_TRY(fa_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, B, H, N, d, scale, causal, block_mask, kv_len, dtype,
+                     stream));
+  return fa_bwd_dq(q, k, v, dO, lse, delta, dq, B, H, N, d, scale, causal, block_mask, kv_len, dtype, stream);
+}
+
+int fa_debug_visits(int which, int B, int H, int N, int d, int causal, const uint8_t* block_mask,
+                    const int32_t* kv_len, int dtype, uint32_t* counts, void* stream) {
+  const Shape s{B, H, N, d, dtype};
+  bool empty = false;
+  if (which < fa::WALK_FWD || which > fa::WALK_DQ) return FA_ERR_ARG;
+  FA_TRY(check_shape(s, block_mask, &empty));
+  if (empty) return FA_OK;
+  if (!counts) return FA_ERR_NULL;
+  if (!aligned(counts, 4)) return FA_ERR_ALIGN;
+  FA_TRY(check_masks(block_mask, kv_len));
+  fa::AttnArgs a = make_args(s, 1.f, causal, block_mask, kv_len);
+  a.counts = counts;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (which == fa::WALK_FWD)
+    e = fa::launch_fwd(a, dtype, d, true, st);
+  else if (which == fa::WALK_DKDV)
+    e = fa::launch_bwd_dkdv(a, dtype, d, true, st);
+  else
+    e = fa::launch_bwd_dq(a, dtype, d, true, st);
+  return hip_status(e);
+}
+
+}  // extern "C"

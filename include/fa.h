@@ -1,0 +1,154 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact IO-aware attention library (libfa.so).
+ *
+ * The library computes exact scaled dot-product attention
+ *     S = scale * Q K^T  (masked entries -inf),   P = rowsoftmax(S),   O = P V
+ * block by block, keeping per query row a running maximum m and normaliser l
+ * so that no N x N matrix is ever written to device memory, and the backward
+ * pass that keeps only O and the per-row log-sum-exp and recomputes S and P
+ * tile by tile.
+ *   - Definition of attention: bornlex.github.io "Flash Attention", section
+ *     "Standard Attention"; FlashAttention reading guide (xyznot.com),
+ *     "Masalah dan Motivasi".
+ *   - Tiling with the running (m, l) statistics: reading guide, "Pelacakan
+ *     Softmax Inkremental" and "Metode" steps 1-4; bornlex "Tiling".
+ *   - Recomputation in the backward pass: reading guide, "Ide Utama";
+ *     bornlex "Recomputation".
+ *   - Block-sparse skipping of zero mask blocks: reading guide, "Ekstensi:
+ *     Block-Sparse FlashAttention".
+ *
+ * Conventions shared by every entry point
+ *   Layout     q, k, v, o, dO, dq, dk, dv are contiguous [B][H][N][d] with d
+ *              innermost, all of the element type given by `dtype`.  lse and
+ *              delta are float32 [B][H][N].  Every pointer must be 16-byte
+ *              aligned.
+ *   dtype      FA_BF16 (bf16 storage, bf16 matrix-core products, float32
+ *              accumulation and softmax) or FA_F32 (float32 throughout; no
+ *              step goes through a narrower type).
+ *   d          64 or 128.
+ *   scale      finite and > 0 (the pages write S = QK^T, i.e. scale = 1).
+ *   causal     nonzero: key j is allowed for query i only if j <= i (queries
+ *              and keys share positions, top-left aligned).
+ *   block_mask NULL, or device uint8 [T][T], T = ceil(N/128), row-major,
+ *              shared by every (b, h): cell (i, j) covers queries
+ *              [128i, 128i+128) and keys [128j, 128j+128); a zero cell is
+ *              skipped (all its scores are -inf).  T <= 2048.
+ *   kv_len     NULL (all N keys valid), or device int32 [B]: for batch b only
+ *              keys j < kv_len[b] are allowed (values are clamped to [0, N]
+ *              on the device).
+ *   Masks combine with AND.  A query row with no allowed key gets O = 0,
+ *   lse = -inf and zero gradient contributions.
+ *   Ownership  every buffer is caller-owned device memory; the library never
+ *              allocates, frees or synchronises, and keeps no state between
+ *              calls.  Calls are stream-ordered on `stream` (a hipStream_t;
+ *              NULL = the default stream) and return before the work ends.
+ *   Errors     arguments are checked before anything is launched; a check
+ *              that fails returns its code and launches nothing.  A launch
+ *              failure returns FA_ERR_HIP.  Faults during execution surface
+ *              at the caller's next synchronisation, as usual for HIP.  The
+ *              library never prints.  Empty problems (B, H or N = 0) return
+ *              FA_OK without launching.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_dtype { FA_BF16 = 0, FA_F32 = 1 };
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,     /* negative size, d not 64/128, T > 2048 or too large */
+  FA_ERR_DTYPE = 3,     /* dtype not FA_BF16 / FA_F32 */
+  FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_WORKSPACE = 5, /* workspace smaller than fa_bwd_workspace_bytes() */
+  FA_ERR_HIP = 6,       /* a HIP launch failed */
+  FA_ERR_ARG = 7        /* scale not finite and > 0, or bad selector */
+};
+
+/*
+ * Forward pass.  Writes o [B,H,N,d] (dtype) and lse [B,H,N] (float32), with
+ * lse_i = m_i + ln(l_i), the natural log of the row normaliser of the scaled
+ * scores; together with O it is all the backward pass needs (the reading
+ * guide's recomputation bullet stores the pair (l, m); lse carries the same
+ * information because P = exp(S - lse)).  Each work-group owns 128 query rows
+ * and walks the allowed 64-key tiles of its row of mask cells in ascending
+ * order, applying the incremental softmax update of "Metode" steps 2-4 with
+ * the division by l deferred to the end.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal,
+           const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* stream);
+
+/*
+ * Bytes of workspace fa_bwd needs: the float32 row terms
+ * delta_i = sum_k dO_ik O_ik, [B,H,N], rounded up to 256.  Linear in N.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
+
+/*
+ * Backward pass for the loss gradient dO: writes dq, dk, dv (dtype).  Runs
+ * fa_bwd_preprocess, fa_bwd_dkdv and fa_bwd_dq in that order on `stream`,
+ * with delta in `workspace` (at least fa_bwd_workspace_bytes bytes, 16-byte
+ * aligned).  o and lse must be the outputs of fa_fwd on the same q, k, v,
+ * scale and masks.  The pages print no backward equations; the ones used
+ * follow from the definition by the chain rule:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta),
+ *   dQ = scale dS K,  dK = scale dS^T Q,  with delta_i = sum_j P_ij dP_ij
+ *   = dO_i . O_i.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+           const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, int causal,
+           const uint8_t* block_mask, const int32_t* kv_len, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward stage 1: delta [B,H,N] float32 = rowsum(dO * O). */
+int fa_bwd_preprocess(const void* o, const void* dO, float* delta,
+                      int B, int H, int N, int d, int dtype, void* stream);
+
+/*
+ * Backward stage 2: dk, dv.  Each work-group owns 128 keys (one mask cell
+ * column) and walks the query tiles that visit it, recomputing S and P from
+ * q, k and lse.
+ */
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                const float* lse, const float* delta, void* dk, void* dv,
+                int B, int H, int N, int d, float scale, int causal,
+                const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* stream);
+
+/*
+ * Backward stage 3: dq.  Each work-group owns 128 queries and walks the same
+ * key tiles as the forward pass, recomputing S, P and dP.
+ */
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+              const float* lse, const float* delta, void* dq,
+              int B, int H, int N, int d, float scale, int causal,
+              const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* stream);
+
+/*
+ * Test hook for the tile-skip schedule.  Runs the tile walk of the forward
+ * (which = 0), dk/dv (1) or dq (2) kernel -- the same iteration code, with the
+ * arithmetic compiled out -- and adds 1 to counts[b][i][j] (uint32, [B][T][T],
+ * zeroed by the caller) for every head h and every visited cell (query cell i,
+ * key cell j).  A cell is visited iff block_mask[i][j] != 0, (not causal or
+ * j <= i) and 128*j < kv_len[b].  d and dtype select the kernel instance.
+ */
+int fa_debug_visits(int which, int B, int H, int N, int d, int causal,
+                    const uint8_t* block_mask, const int32_t* kv_len, int dtype,
+                    uint32_t* counts, void* stream);
+
+/* Static, NUL-terminated name of a status code. */
+const char* fa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,79 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run the
+library through its C ABI binding, and compare against the fp64 oracle.
+
+Tolerances (stated for the hot path of exact attention):
+  float32 inputs: max |dO| <= 1e-5, max |dlse| <= 1e-5, gradients max|d|/max|g| <= 1e-5
+  bf16 inputs:    max |dO| <= 1e-2 and mean |dO| <= 1e-3, max |dlse| <= 1e-3,
+                  gradients max|d| / max|g_oracle| <= 5e-2 per tensor
+"""
+import sys
+
+import numpy as np
+
+TOL = {
+    "f32": dict(o_max=1e-5, o_mean=1e-5, lse=1e-5, grad=1e-5),
+    "bf16": dict(o_max=1e-2, o_mean=1e-3, lse=1e-3, grad=5e-2),
+}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype == "bf16":
+        return t.to("cuda", torch.bfloat16)
+    return t.to("cuda", torch.float32)
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def run_gpu(inp, backward=True):
+    """fa_fwd (+ fa_bwd) on the inputs of workloads.make_inputs; returns numpy fp64 arrays."""
+    import torch
+
+    import exact_io_aware_flashattention_amd as fa
+    dt = inp["dtype"]
+    q, k, v, do = (to_dev(inp[n], dt) for n in ("q", "k", "v", "do"))
+    bm = None if inp["block_mask"] is None else torch.from_numpy(inp["block_mask"]).cuda()
+    kl = None if inp["kv_len"] is None else torch.from_numpy(inp["kv_len"].astype(np.int32)).cuda()
+    o, lse = fa.fa_fwd(q, k, v, scale=inp["scale"], causal=inp["causal"], block_mask=bm, kv_len=kl)
+    out = {}
+    if backward:
+        dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, scale=inp["scale"], causal=inp["causal"],
+                               block_mask=bm, kv_len=kl)
+    torch.cuda.synchronize()
+    out["o"], out["lse"] = host(o), lse.cpu().numpy().astype(np.float64)
+    if backward:
+        out["dq"], out["dk"], out["dv"] = host(dq), host(dk), host(dv)
+    return out
+
+
+def compare_forward(o, lse, o_ref, lse_ref, dtype, what=""):
+    tol = TOL[dtype]
+    fin_ref = np.isfinite(lse_ref)
+    assert np.array_equal(fin_ref, np.isfinite(lse)), f"{what}: lse -inf pattern differs"
+    assert np.all(np.isfinite(o)), f"{what}: non-finite O"
+    d = np.abs(o - o_ref)
+    dl = np.abs(lse[fin_ref] - lse_ref[fin_ref]) if fin_ref.any() else np.zeros(1)
+    say(f"  {what} O max {d.max():.3e} mean {d.mean():.3e}  lse max {dl.max():.3e}")
+    assert d.max() <= tol["o_max"], f"{what}: max|dO| {d.max():.3e}"
+    assert d.mean() <= tol["o_mean"], f"{what}: mean|dO| {d.mean():.3e}"
+    assert dl.max() <= tol["lse"], f"{what}: max|dlse| {dl.max():.3e}"
+    # rows with no allowed key: O = 0 exactly
+    if (~fin_ref).any():
+        assert np.all(o[~fin_ref] == 0)
+
+
+def compare_grad(g, g_ref, dtype, name):
+    tol = TOL[dtype]["grad"]
+    assert np.all(np.isfinite(g)), f"{name}: non-finite gradient"
+    scale = max(np.abs(g_ref).max(), 1e-30)
+    e = np.abs(g - g_ref).max() / scale
+    say(f"  {name} normalised max err {e:.3e} (max|g| {scale:.3e})")
+    assert e <= tol, f"{name}: {e:.3e} > {tol}"

@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle on the
+same seeded inputs.  Small shapes are compared element by element against the
+full dense oracle; the five workloads at full size are compared on sampled
+heads, rows and key columns with the gathered (sparse) form of the oracle."""
+import numpy as np
+import pytest
+
+from oracle import attention, sparse
+from workloads import WORKLOADS, band_random_mask, draw_kv_len, draw_qkvdo, make_inputs
+
+from gpu_cases import compare_forward, compare_grad, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_io_aware_flashattention_amd as fa
+    fa.load_library()
+
+
+def small_inputs(B, H, N, d, dtype, causal, kv=None, mask=None, seed=0, sigma=1.0, scale=None):
+    q, k, v, do = draw_qkvdo(B, H, N, d, dtype, sigma, seed)
+    T = -(-N // 128)
+    kv_len = None
+    if isinstance(kv, str):
+        kv_len = draw_kv_len(B, 1, N, 1000 + seed)
+    elif kv is not None:
+        kv_len = np.asarray(kv, np.int32)
+    bm = None
+    if isinstance(mask, str) and mask == "band":
+        bm = band_random_mask(T, 2000 + seed, n_random=1)
+    elif isinstance(mask, str) and mask == "bern":
+        rng = np.random.Generator(np.random.PCG64(3000 + seed))
+        bm = (rng.random((T, T)) < 0.5).astype(np.uint8)
+        bm[:, 0] = 1
+    elif mask is not None:
+        bm = np.asarray(mask, np.uint8)
+    return dict(q=q, k=k, v=v, do=do, kv_len=kv_len, block_mask=bm, B=B, H=H, N=N, d=d, dtype=dtype,
+                causal=causal, scale=(1.0 / np.sqrt(d)) if scale is None else scale)
+
+
+def check_full(inp, what, backward=True):
+    say(f"case {what}: B={inp['B']} H={inp['H']} N={inp['N']} d={inp['d']} {inp['dtype']} "
+        f"causal={inp['causal']} kv={inp['kv_len'] is not None} mask={inp['block_mask'] is not None}")
+    out = run_gpu(inp, backward)
+    kw = dict(causal=inp["causal"], block_mask=inp["block_mask"], kv_len=inp["kv_len"])
+    O, lse = attention.forward(inp["q"], inp["k"], inp["v"], inp["scale"], **kw)
+    compare_forward(out["o"], out["lse"], O, lse, inp["dtype"], what)
+    if backward:
+        g = attention.backward(inp["q"], inp["k"], inp["v"], inp["do"], inp["scale"], **kw)
+        for name, a, r in zip(("dq", "dk", "dv"), (out["dq"], out["dk"], out["dv"]), g):
+            compare_grad(a, r, inp["dtype"], f"{what} {name}")
+    return out
+
+
+SMALL = [
+    # B, H, N, d, dtype, causal, kv, mask
+    (1, 1, 1, 64, "bf16", False, None, None),
+    (1, 1, 1, 128, "f32", True, None, None),
+    (1, 2, 63, 64, "bf16", True, None, None),
+    (2, 1, 64, 128, "bf16", False, None, None),
+    (1, 2, 65, 64, "f32", False, None, None),
+    (1, 2, 127, 128, "bf16", True, None, None),
+    (2, 2, 129, 64, "bf16", True, "rand", None),
+    (1, 3, 200, 128, "bf16", False, "rand", None),
+    (2, 2, 256, 64, "bf16", True, None, "bern"),
+    (1, 2, 300, 128, "f32", True, "rand", "band"),
+    (3, 2, 333, 64, "bf16", False, "rand", "bern"),
+    (1, 2, 513, 128, "bf16", True, None, "band"),
+    (1, 1, 1000, 64, "f32", True, None, None),
+    (2, 1, 1000, 128, "bf16", False, "rand", None),
+    (1, 1, 640, 64, "bf16", False, None, "band"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B{}H{}N{}d{}{}{}{}{}".format(
+    c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "", "k" if c[6] else "", "m" if c[7] else ""))
+def test_small_shapes(case):
+    B, H, N, d, dt, causal, kv, mask = case
+    check_full(small_inputs(B, H, N, d, dt, causal, kv, mask, seed=N + d + B), str(case))
+
+
+def test_tiny_exact_config_fp32():
+    """Workload 1 at its own size: fp32, B=1 H=2 N=128 d=64, no mask."""
+    check_full(make_inputs(WORKLOADS[1]), "workload-1")
+
+
+def test_fully_masked_rows():
+    """kv_len = 0 (no key at all), kv_len > N (clamped), and a mask row of zeros."""
+    inp = small_inputs(3, 2, 256, 64, "bf16", False, kv=[0, 5000, 129], seed=5)
+    out = check_full(inp, "kv0")
+    assert np.all(out["o"][0] == 0) and np.all(out["lse"][0] == -np.inf)
+    assert np.all(out["dq"][0] == 0) and np.all(out["dk"][0] == 0) and np.all(out["dv"][0] == 0)
+    bm = np.ones((2, 2), np.uint8)
+    bm[1, :] = 0
+    inp = small_inputs(1, 2, 256, 128, "bf16", True, mask=bm, seed=6)
+    out = check_full(inp, "mask-empty-row")
+    assert np.all(out["lse"][:, :, 128:] == -np.inf)
+
+
+def test_large_scores_stay_finite():
+    """Scores around +-1e3 (sigma 6, d 64, scale 1): the running max keeps exp finite."""
+    inp = small_inputs(1, 2, 384, 64, "f32", True, seed=8, sigma=6.0, scale=1.0)
+    check_full(inp, "large-scores")
+
+
+def test_deterministic_repeat():
+    inp = small_inputs(1, 4, 700, 128, "bf16", True, "rand", "bern", seed=9)
+    a = run_gpu(inp)
+    b = run_gpu(inp)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_empty_problem_is_a_no_op():
+    import torch
+
+    import exact_io_aware_flashattention_amd as fa
+    q = torch.zeros((0, 2, 16, 64), dtype=torch.bfloat16, device="cuda")
+    o, lse = fa.fa_fwd(q, q, q)
+    assert o.shape == q.shape and lse.shape == (0, 2, 16)
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def _sample_heads(B, H, n, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pairs = {(0, 0), (B - 1, H - 1)}
+    while len(pairs) < min(n, B * H):
+        pairs.add((int(rng.integers(B)), int(rng.integers(H))))
+    return sorted(pairs)
+
+
+def _check_heads_dense(inp, out, pairs, what):
+    for (b, h) in pairs:
+        L = None if inp["kv_len"] is None else int(inp["kv_len"][b])
+        args = (inp["q"][b, h], inp["k"][b, h], inp["v"][b, h])
+        O, lse = attention.head_forward(*args, inp["scale"], causal=inp["causal"], kv_len=L,
+                                        block_mask=inp["block_mask"])
+        compare_forward(out["o"][b, h], out["lse"][b, h], O, lse, inp["dtype"], f"{what} b{b}h{h}")
+        g = attention.head_backward(*args, inp["do"][b, h], inp["scale"], inp["causal"], inp["block_mask"], L)
+        for name, a, r in zip(("dq", "dk", "dv"), (out["dq"], out["dk"], out["dv"]), g):
+            compare_grad(a[b, h], r, inp["dtype"], f"{what} b{b}h{h} {name}")
+
+
+@pytest.mark.parametrize("key", [2, 3])
+def test_workload_full_size_sampled_heads(key):
+    inp = make_inputs(WORKLOADS[key])
+    say(f"workload {key} ({WORKLOADS[key].name}) full size")
+    out = run_gpu(inp)
+    for n in ("o", "dq", "dk", "dv"):
+        assert np.all(np.isfinite(out[n])), n
+    _check_heads_dense(inp, out, _sample_heads(inp["B"], inp["H"], 6, key), f"w{key}")
+
+
+@pytest.mark.parametrize("key", [4, 5])
+def test_workload_long_sequence_sampled(key):
+    """N = 16K causal and N = 64K block-sparse: sampled rows of O, lse and dQ and
+    sampled key columns of dK, dV on two heads, against the gathered oracle."""
+    inp = make_inputs(WORKLOADS[key])
+    say(f"workload {key} ({WORKLOADS[key].name}) full size")
+    out = run_gpu(inp)
+    for n in ("o", "dq", "dk", "dv"):
+        assert np.all(np.isfinite(out[n])), n
+    N = inp["N"]
+    rng = np.random.Generator(np.random.PCG64(77 + key))
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, N // 2, N - 129, N - 1], rng.integers(0, N, 57)]))
+    cols = np.unique(np.concatenate([[0, 1, 127, 128, N - 1], rng.integers(0, N, 27)]))
+    kw = dict(causal=inp["causal"], block_mask=inp["block_mask"], kv_len=None)
+    for h in (0, inp["H"] - 1):
+        Q, K, V, dO = (inp[n][0, h] for n in ("q", "k", "v", "do"))
+        O, lse = sparse.head_forward_rows(Q, K, V, inp["scale"], rows, **kw)
+        compare_forward(out["o"][0, h][rows], out["lse"][0, h][rows], O, lse, "bf16", f"w{key} h{h} rows")
+        dQ = sparse.head_backward_rows(Q, K, V, dO, inp["scale"], rows, **kw)
+        # normalised by the largest oracle value among the sampled entries
+        compare_grad(out["dq"][0, h][rows], dQ, "bf16", f"w{key} h{h} dq rows")
+        _, dK, dV = sparse.head_backward(Q, K, V, dO, inp["scale"], key_cols=cols, **kw)
+        compare_grad(out["dk"][0, h][cols], dK, "bf16", f"w{key} h{h} dk cols")
+        compare_grad(out["dv"][0, h][cols], dV, "bf16", f"w{key} h{h} dv cols")
