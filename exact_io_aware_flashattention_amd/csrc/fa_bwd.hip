@@ -153,13 +153,16 @@ __device__ __forceinline__ void store_acc_rows(T* base, int row, int N, const f3
 template <typename T, int D>
 struct DkdvCfg {
   using TL = Tile64<T, D>;
+  // d = 128 needs more than 256 registers per wave (two fp32 accumulators of
+  // 32 x 128 plus K, V fragments): one wave per SIMD, double-buffered LDS.
+  static constexpr int OCC = (sizeof(T) == 2 && D == 64) ? 2 : 1;
   static constexpr int STAGE = 2 * TL::ROW_ELEMS + 2 * TL::TR_ELEMS;   // Q, dO row-major + transposed
   static constexpr int STAGE_BYTES = STAGE * (int)sizeof(T) + 2 * 64 * 4;
-  static constexpr int NSTAGE = (2 * STAGE_BYTES + MAX_T * 4 <= 160 * 1024) ? 2 : 1;
+  static constexpr int NSTAGE = (2 * STAGE_BYTES + MAX_T * 4 <= 160 * 1024 / OCC) ? 2 : 1;
 };
 
 template <typename T, int D, bool WALK_ONLY>
-__global__ __launch_bounds__(NT) void bwd_dkdv_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DkdvCfg<T, D>::OCC, DkdvCfg<T, D>::OCC))) void bwd_dkdv_kernel(AttnArgs a) {
   using TL = Tile64<T, D>;
   using CF = DkdvCfg<T, D>;
   constexpr int CW = TL::CW;
@@ -330,11 +333,11 @@ struct DqCfg {
   using TL = Tile64<T, D>;
   static constexpr int STAGE = 2 * TL::ROW_ELEMS + TL::TR_ELEMS;   // K, V row-major + K transposed
   static constexpr int STAGE_BYTES = STAGE * (int)sizeof(T);
-  static constexpr int NSTAGE = (2 * STAGE_BYTES + MAX_T * 4 <= 160 * 1024) ? 2 : 1;
+  static constexpr int NSTAGE = (2 * STAGE_BYTES + MAX_T * 4 <= 160 * 1024 / Occ<T>::W) ? 2 : 1;
 };
 
 template <typename T, int D, bool WALK_ONLY>
-__global__ __launch_bounds__(NT) void bwd_dq_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occ<T>::W, Occ<T>::W))) void bwd_dq_kernel(AttnArgs a) {
   using TL = Tile64<T, D>;
   using CF = DqCfg<T, D>;
   constexpr int CW = TL::CW;

@@ -37,6 +37,10 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr float TAU = 8.0f;    // the running max is refreshed only when a tile
                                // exceeds it by more than 2^TAU (see softmax_update)
 
+// Waves per SIMD the bf16 kernels are register-limited to: two resident waves
+// let one wave's softmax VALU work overlap the other's matrix-core work.
+template <typename T> struct Occ { static constexpr int W = sizeof(T) == 2 ? 2 : 1; };
+
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float pos_inf() { return __builtin_inff(); }
 

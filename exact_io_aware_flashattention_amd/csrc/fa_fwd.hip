@@ -43,7 +43,7 @@ struct FwdTile {
 };
 
 template <typename T, int D, bool WALK_ONLY>
-__global__ __launch_bounds__(NT) void fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occ<T>::W, Occ<T>::W))) void fwd_kernel(AttnArgs a) {
   using TL = FwdTile<T, D>;
   constexpr int CW = TL::CW;
   __shared__ __attribute__((aligned(16))) T smem[WALK_ONLY ? 8 : 2 * TL::STAGE];
