@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bf16.hip"]
 ARCH = "gfx950"
 
 COMMON = [
@@ -39,7 +39,7 @@ def _run(cmd):
     return r.stdout
 
 
-def build(jobs: int = 3, extra_flags=()) -> str:
+def build(jobs: int = 4, extra_flags=()) -> str:
     os.makedirs(OBJ, exist_ok=True)
     cc = hipcc()
     cmds = []

@@ -1,0 +1,482 @@
+// bf16 kernels: forward, dK/dV and dQ.
+//
+// The arithmetic is the same as in the float kernels (fa_fwd.hip, fa_bwd.hip):
+//   forward  FlashAttention reading guide, "Metode" steps 1-4, with the
+//            division by l deferred to the end and a lazily refreshed row max;
+//   backward dV = P^T dO, dP = dO V^T, dS = P (dP - delta), dQ = scale dS K,
+//            dK = scale dS^T Q, recomputing S and P from lse (reading guide,
+//            "Ide Utama", recomputation bullet).
+// What differs is how tiles reach the matrix cores on gfx950: every K, V, Q
+// and dO tile travels HBM -> LDS by buffer-to-LDS loads (no register staging,
+// no LDS writes by the waves), is stored once, row-major and swizzled, and is
+// read back either by rows (ds_read_b128) or transposed (ds_read_b64_tr_b16)
+// for the products that contract over the tile rows.  All three kernels run
+// two waves per SIMD (at most 256 registers per wave) so one wave's softmax
+// and mask work overlaps the other wave's matrix-core work.
+#include "fa_device.hpp"
+#include "fa_kernels.hpp"
+#include "fa_tile.hpp"
+#include "fa_walk.hpp"
+
+namespace fa {
+
+// Scores of one 32 x 32 block in accumulator layout: register r of lane l
+// belongs to the key/query pair (8*(r/4) + 4*h + r%4, l % 32).
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+__device__ __forceinline__ void zero(f32x16& x) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) x[r] = 0.f;
+}
+
+// ---------------------------------------------------------------- forward
+
+template <int D>
+struct FwdB {
+  static constexpr int BC = 64;                 // keys per tile
+  static constexpr int TILE = BC * D * 2;       // bytes of one K or V tile
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int SSTEPS = D / 16;
+  static constexpr int NB = D / 32;
+};
+
+template <int D, bool WALK_ONLY>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(AttnArgs a) {
+  using C = FwdB<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[WALK_ONLY ? 16 : 2 * C::STAGE];
+  __shared__ int cell_list[MAX_T];
+  __shared__ int scratch4[4];
+
+  const int N = a.N;
+  const int T_cells = (N + CELL - 1) / CELL;
+  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int bh = L / T_cells, tq = L - bh * T_cells;
+  const int qi = a.causal ? T_cells - 1 - tq : tq;   // heaviest causal rows first
+  const int b = bh / a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+
+  const int kvl = clamp_kv_len(a, b);
+  const int q_lo = qi * CELL, q_hi = min(q_lo + CELL, N);
+  const int kv_end = a.causal ? min(kvl, q_hi) : kvl;
+  const Walk walk = row_walk(a, qi, kv_end, T_cells, cell_list, scratch4, 6);
+
+  if constexpr (WALK_ONLY) {
+    for (int it = 0; it < walk.ntiles; ++it)
+      if (tid == 0 && walk.first_of_cell(it))
+        atomicAdd(&a.counts[((size_t)b * T_cells + qi) * T_cells + walk.cell(it >> 1)], 1u);
+    return;
+  } else {
+    const size_t head = (size_t)bh * N * D;
+    const bf16* Q = reinterpret_cast<const bf16*>(a.q) + head;
+    const bf16* K = reinterpret_cast<const bf16*>(a.k) + head;
+    const bf16* V = reinterpret_cast<const bf16*>(a.v) + head;
+    bf16* O = reinterpret_cast<bf16*>(a.out0) + head;
+    const auto rk = head_rsrc(K, N, D), rv = head_rsrc(V, N, D);
+
+    const int qw0 = q_lo + wave * 32;
+    const int myq = qw0 + l32;
+    const bool wave_has_rows = qw0 < N;
+
+    u32x4 qf[C::SSTEPS];
+#pragma unroll
+    for (int s = 0; s < C::SSTEPS; ++s)
+      qf[s] = (myq < N) ? ld16(Q + (size_t)myq * D + s * 16 + 8 * h) : u32x4{0, 0, 0, 0};
+    f32x16 acc[C::NB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) zero(acc[nb]);
+    float m_run = neg_inf(), l_run = 0.f;
+
+    auto issue = [&](int it) {
+      unsigned char* st = smem + (it & 1) * C::STAGE;
+      const int kb0 = walk.tile_start(it);
+      tile_load<D, 64>(rk, kb0, st);
+      tile_load<D, 64>(rv, kb0, st + C::TILE);
+    };
+    if (walk.ntiles > 0) issue(0);
+
+    for (int it = 0; it < walk.ntiles; ++it) {
+      wait_loads();
+      __syncthreads();
+      if (it + 1 < walk.ntiles) issue(it + 1);
+      const int kb0 = walk.tile_start(it);
+      const unsigned char* Ks = smem + (it & 1) * C::STAGE;
+      const unsigned char* Vs = Ks + C::TILE;
+      if (!wave_has_rows || (a.causal && kb0 > qw0 + 31)) continue;
+
+      // step 1: S^T = K Q^T, two 32-key halves
+      f32x16 s[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        zero(s[sb]);
+#pragma unroll
+        for (int st = 0; st < C::SSTEPS; ++st)
+          mma(s[sb], as_bf16x8(row_chunk<D>(Ks, 32 * sb + l32, 2 * st + h)), as_bf16x8(qf[st]));
+      }
+      if ((kb0 + C::BC > kvl) || (a.causal && kb0 + C::BC - 1 > qw0)) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb0 + 32 * sb + acc_row(r, h);
+            if (key >= kvl || (a.causal && key > myq)) s[sb][r] = neg_inf();
+          }
+      }
+      // step 2: tile row max (two lane halves hold disjoint keys of a query)
+      float mx = neg_inf();
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+      mx = max_halves(mx);
+      const float mt = mx * a.c;
+      // step 3: refresh the running max only when a score exceeds it by > 2^TAU
+      if (wave_any(mt > m_run + TAU)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[nb][r] *= alpha;
+        m_run = m_new;
+      }
+      const float mu = (m_run == neg_inf()) ? 0.f : m_run;
+      float ls = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], a.c, -mu));
+          s[sb][r] = p;
+          ls += p;
+        }
+      l_run += ls;
+      // step 4: O^T += V^T P~^T, V^T read transposed from the row-major tile
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const PackedB pb = pack_bf16(s[sb]);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) mma(acc[nb], tr_operand<D>(Vs, 32 * sb + 16 * mm, 32 * nb), pb.p[mm]);
+      }
+    }
+
+    const float l_tot = sum_halves(l_run);
+    if (myq < N) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      bf16* orow = O + (size_t)myq * D;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4(orow + 32 * nb + 8 * g + 4 * h, acc[nb][4 * g] * inv, acc[nb][4 * g + 1] * inv,
+                 acc[nb][4 * g + 2] * inv, acc[nb][4 * g + 3] * inv);
+      if (h == 0) a.lse[(size_t)bh * N + myq] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * LN2 : neg_inf();
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dK / dV
+
+template <int D>
+struct DkdvB {
+  static constexpr int BQ = D == 128 ? 32 : 64;     // queries per stage
+  static constexpr int TSH = D == 128 ? 5 : 6;
+  static constexpr int QS = BQ / 32;
+  static constexpr int TILE = BQ * D * 2;           // one Q or dO tile (bytes)
+  static constexpr int STAGE = 2 * TILE + 2 * BQ * 4;   // Q, dO, lse*log2e, delta
+  static constexpr int VRES = CELL * D * 2;         // V of the work-group's 128 keys
+  static constexpr int SSTEPS = D / 16;
+  static constexpr int NB = D / 32;
+};
+
+template <int D, bool WALK_ONLY>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_bf16_kernel(AttnArgs a) {
+  using C = DkdvB<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[WALK_ONLY ? 16 : C::VRES + 2 * C::STAGE];
+  __shared__ int cell_list[MAX_T];
+  __shared__ int scratch4[4];
+
+  const int N = a.N;
+  const int T_cells = (N + CELL - 1) / CELL;
+  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int bh = L / T_cells, kj = L - bh * T_cells;
+  const int b = bh / a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int kvl = clamp_kv_len(a, b);
+  const Walk walk = col_walk(a, kj, kvl, T_cells, cell_list, scratch4, C::TSH);
+
+  if constexpr (WALK_ONLY) {
+    for (int it = 0; it < walk.ntiles; ++it)
+      if (tid == 0 && walk.first_of_cell(it))
+        atomicAdd(&a.counts[((size_t)b * T_cells + walk.cell(it >> (7 - C::TSH))) * T_cells + kj], 1u);
+    return;
+  } else {
+    const size_t head = (size_t)bh * N * D;
+    const bf16* Kg = reinterpret_cast<const bf16*>(a.k) + head;
+    const float* lse_g = a.lse + (size_t)bh * N;
+    const float* del_g = a.delta + (size_t)bh * N;
+    const auto rq = head_rsrc(reinterpret_cast<const bf16*>(a.q) + head, N, D);
+    const auto rg = head_rsrc(reinterpret_cast<const bf16*>(a.dO) + head, N, D);
+    const auto rv = head_rsrc(reinterpret_cast<const bf16*>(a.v) + head, N, D);
+
+    const int kw0 = kj * CELL + wave * 32;   // first key of this wave
+    const int myk = kw0 + l32;               // the key this lane owns
+    const bool wave_has_keys = kw0 < kvl;
+    unsigned char* Vs = smem;
+
+    u32x4 kf[C::SSTEPS];
+#pragma unroll
+    for (int s = 0; s < C::SSTEPS; ++s)
+      kf[s] = myk < N ? ld16(Kg + (size_t)myk * D + s * 16 + 8 * h) : u32x4{0, 0, 0, 0};
+    f32x16 dk[C::NB], dv[C::NB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+      zero(dk[nb]);
+      zero(dv[nb]);
+    }
+
+    float st_l = 0.f, st_d = 0.f;   // this thread's row statistics of the next tile
+    auto issue = [&](int it) {
+      unsigned char* st = smem + C::VRES + (it & 1) * C::STAGE;
+      const int q0 = walk.tile_start(it);
+      tile_load<D, C::BQ>(rq, q0, st);
+      tile_load<D, C::BQ>(rg, q0, st + C::TILE);
+      if (tid < C::BQ) {
+        const int q = q0 + tid;
+        const float l = q < N ? lse_g[q] : neg_inf();
+        st_l = (l == neg_inf()) ? pos_inf() : l * LOG2E;   // empty rows and rows past N get P = 0
+        st_d = q < N ? del_g[q] : 0.f;
+      }
+    };
+    if (walk.ntiles > 0) {
+      tile_load<D, CELL>(rv, kj * CELL, Vs);
+      issue(0);
+    }
+
+    for (int it = 0; it < walk.ntiles; ++it) {
+      wait_loads();
+      unsigned char* st = smem + C::VRES + (it & 1) * C::STAGE;
+      float* stats = reinterpret_cast<float*>(st + 2 * C::TILE);
+      if (tid < C::BQ) {
+        stats[tid] = st_l;
+        stats[C::BQ + tid] = st_d;
+      }
+      __syncthreads();
+      if (it + 1 < walk.ntiles) issue(it + 1);
+      const int q0 = walk.tile_start(it);
+      const unsigned char* Qs = st;
+      const unsigned char* dOs = st + C::TILE;
+      if (!wave_has_keys || (a.causal && kw0 > q0 + C::BQ - 1)) continue;
+      const bool edge = (kw0 + 32 > kvl) || (a.causal && kw0 + 31 > q0);
+#pragma unroll
+      for (int qs = 0; qs < C::QS; ++qs) {
+        // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys (lane = key)
+        f32x16 s, dp;
+        zero(s);
+        zero(dp);
+#pragma unroll
+        for (int k = 0; k < C::SSTEPS; ++k) {
+          mma(s, as_bf16x8(row_chunk<D>(Qs, 32 * qs + l32, 2 * k + h)), as_bf16x8(kf[k]));
+          mma(dp, as_bf16x8(row_chunk<D>(dOs, 32 * qs + l32, 2 * k + h)),
+              as_bf16x8(row_chunk<D>(Vs, wave * 32 + l32, 2 * k + h)));
+        }
+        // P = exp2(s c - lse log2 e), dS = P (dP - delta); register r <-> query 32 qs + acc_row(r, h)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int qq = 32 * qs + 8 * g + 4 * h;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(stats + qq);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(stats + C::BQ + qq);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -l4[e]));
+            if (edge && (myk >= kvl || (a.causal && myk > q0 + qq + e))) p = 0.f;
+            s[r] = p;
+            dp[r] = p * (dp[r] - d4[e]);
+          }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS, the transposed operands read from the row-major tiles
+        const PackedB pb = pack_bf16(s), db = pack_bf16(dp);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            mma(dv[nb], tr_operand<D>(dOs, 32 * qs + 16 * mm, 32 * nb), pb.p[mm]);
+            mma(dk[nb], tr_operand<D>(Qs, 32 * qs + 16 * mm, 32 * nb), db.p[mm]);
+          }
+      }
+    }
+
+    if (myk < N) {
+      bf16* dkp = reinterpret_cast<bf16*>(a.out0) + head + (size_t)myk * D;
+      bf16* dvp = reinterpret_cast<bf16*>(a.out1) + head + (size_t)myk * D;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = 32 * nb + 8 * g + 4 * h;
+          store4(dkp + c, dk[nb][4 * g] * a.scale, dk[nb][4 * g + 1] * a.scale, dk[nb][4 * g + 2] * a.scale,
+                 dk[nb][4 * g + 3] * a.scale);
+          store4(dvp + c, dv[nb][4 * g], dv[nb][4 * g + 1], dv[nb][4 * g + 2], dv[nb][4 * g + 3]);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+
+template <int D>
+struct DqB {
+  static constexpr int BC = 64;
+  static constexpr int TILE = BC * D * 2;
+  static constexpr int STAGE = 2 * TILE;        // K, V
+  static constexpr int SSTEPS = D / 16;
+  static constexpr int NB = D / 32;
+};
+
+template <int D, bool WALK_ONLY>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_bf16_kernel(AttnArgs a) {
+  using C = DqB<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[WALK_ONLY ? 16 : 2 * C::STAGE];
+  __shared__ int cell_list[MAX_T];
+  __shared__ int scratch4[4];
+
+  const int N = a.N;
+  const int T_cells = (N + CELL - 1) / CELL;
+  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int bh = L / T_cells, tq = L - bh * T_cells;
+  const int qi = a.causal ? T_cells - 1 - tq : tq;
+  const int b = bh / a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int kvl = clamp_kv_len(a, b);
+  const int q_lo = qi * CELL, q_hi = min(q_lo + CELL, N);
+  const int kv_end = a.causal ? min(kvl, q_hi) : kvl;
+  const Walk walk = row_walk(a, qi, kv_end, T_cells, cell_list, scratch4, 6);
+
+  if constexpr (WALK_ONLY) {
+    for (int it = 0; it < walk.ntiles; ++it)
+      if (tid == 0 && walk.first_of_cell(it))
+        atomicAdd(&a.counts[((size_t)b * T_cells + qi) * T_cells + walk.cell(it >> 1)], 1u);
+    return;
+  } else {
+    const size_t head = (size_t)bh * N * D;
+    const bf16* Qg = reinterpret_cast<const bf16*>(a.q) + head;
+    const bf16* dOg = reinterpret_cast<const bf16*>(a.dO) + head;
+    const auto rk = head_rsrc(reinterpret_cast<const bf16*>(a.k) + head, N, D);
+    const auto rv = head_rsrc(reinterpret_cast<const bf16*>(a.v) + head, N, D);
+
+    const int qw0 = q_lo + wave * 32;
+    const int myq = qw0 + l32;
+    const bool wave_has_rows = qw0 < N;
+
+    u32x4 qf[C::SSTEPS], gf[C::SSTEPS];
+#pragma unroll
+    for (int s = 0; s < C::SSTEPS; ++s) {
+      const bool ok = myq < N;
+      qf[s] = ok ? ld16(Qg + (size_t)myq * D + s * 16 + 8 * h) : u32x4{0, 0, 0, 0};
+      gf[s] = ok ? ld16(dOg + (size_t)myq * D + s * 16 + 8 * h) : u32x4{0, 0, 0, 0};
+    }
+    float lse2 = pos_inf(), del = 0.f;
+    if (myq < N) {
+      const float l = a.lse[(size_t)bh * N + myq];
+      lse2 = (l == neg_inf()) ? pos_inf() : l * LOG2E;
+      del = a.delta[(size_t)bh * N + myq];
+    }
+    f32x16 dq[C::NB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) zero(dq[nb]);
+
+    auto issue = [&](int it) {
+      unsigned char* st = smem + (it & 1) * C::STAGE;
+      const int kb0 = walk.tile_start(it);
+      tile_load<D, 64>(rk, kb0, st);
+      tile_load<D, 64>(rv, kb0, st + C::TILE);
+    };
+    if (walk.ntiles > 0) issue(0);
+
+    for (int it = 0; it < walk.ntiles; ++it) {
+      wait_loads();
+      __syncthreads();
+      if (it + 1 < walk.ntiles) issue(it + 1);
+      const int kb0 = walk.tile_start(it);
+      const unsigned char* Ks = smem + (it & 1) * C::STAGE;
+      const unsigned char* Vs = Ks + C::TILE;
+      if (!wave_has_rows || (a.causal && kb0 > qw0 + 31)) continue;
+      const bool edge = (kb0 + C::BC > kvl) || (a.causal && kb0 + C::BC - 1 > qw0);
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries (lane = query)
+        f32x16 s, dp;
+        zero(s);
+        zero(dp);
+#pragma unroll
+        for (int k = 0; k < C::SSTEPS; ++k) {
+          mma(s, as_bf16x8(row_chunk<D>(Ks, 32 * sb + l32, 2 * k + h)), as_bf16x8(qf[k]));
+          mma(dp, as_bf16x8(row_chunk<D>(Vs, 32 * sb + l32, 2 * k + h)), as_bf16x8(gf[k]));
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -lse2));
+          if (edge) {
+            const int key = kb0 + 32 * sb + acc_row(r, h);
+            if (key >= kvl || (a.causal && key > myq)) p = 0.f;
+          }
+          dp[r] = p * (dp[r] - del);
+        }
+        // dQ^T += K^T dS^T, K^T read transposed from the row-major tile
+        const PackedB db = pack_bf16(dp);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) mma(dq[nb], tr_operand<D>(Ks, 32 * sb + 16 * mm, 32 * nb), db.p[mm]);
+      }
+    }
+
+    if (myq < N) {
+      bf16* p = reinterpret_cast<bf16*>(a.out0) + head + (size_t)myq * D;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4(p + 32 * nb + 8 * g + 4 * h, dq[nb][4 * g] * a.scale, dq[nb][4 * g + 1] * a.scale,
+                 dq[nb][4 * g + 2] * a.scale, dq[nb][4 * g + 3] * a.scale);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <template <int, bool> class KER, int D>
+struct Launch;
+
+#define FA_DEFINE_LAUNCH(NAME, KERNEL)                                                                   \
+  template <int D>                                                                                       \
+  static hipError_t NAME(const AttnArgs& a, bool walk_only, hipStream_t s) {                            \
+    const long long nwg = (long long)((a.N + CELL - 1) / CELL) * a.H * a.B;                              \
+    if (walk_only)                                                                                       \
+      hipLaunchKernelGGL((KERNEL<D, true>), dim3((unsigned)nwg), dim3(NT), 0, s, a);                     \
+    else                                                                                                 \
+      hipLaunchKernelGGL((KERNEL<D, false>), dim3((unsigned)nwg), dim3(NT), 0, s, a);                    \
+    return hipGetLastError();                                                                            \
+  }
+
+FA_DEFINE_LAUNCH(launch_fwd_b, fwd_bf16_kernel)
+FA_DEFINE_LAUNCH(launch_dkdv_b, dkdv_bf16_kernel)
+FA_DEFINE_LAUNCH(launch_dq_b, dq_bf16_kernel)
+
+hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s) {
+  return d == 64 ? launch_fwd_b<64>(a, walk_only, s) : launch_fwd_b<128>(a, walk_only, s);
+}
+hipError_t launch_dkdv_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s) {
+  return d == 64 ? launch_dkdv_b<64>(a, walk_only, s) : launch_dkdv_b<128>(a, walk_only, s);
+}
+hipError_t launch_dq_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s) {
+  return d == 64 ? launch_dq_b<64>(a, walk_only, s) : launch_dq_b<128>(a, walk_only, s);
+}
+
+}  // namespace fa

@@ -506,14 +506,12 @@ hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int d, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int dtype, int d, bool walk_only, hipStream_t s) {
-  if (dtype == 0)
-    return d == 64 ? launch_dkdv_t<bf16, 64>(a, walk_only, s) : launch_dkdv_t<bf16, 128>(a, walk_only, s);
+  if (dtype == 0) return launch_dkdv_bf16(a, d, walk_only, s);
   return d == 64 ? launch_dkdv_t<float, 64>(a, walk_only, s) : launch_dkdv_t<float, 128>(a, walk_only, s);
 }
 
 hipError_t launch_bwd_dq(const AttnArgs& a, int dtype, int d, bool walk_only, hipStream_t s) {
-  if (dtype == 0)
-    return d == 64 ? launch_dq_t<bf16, 64>(a, walk_only, s) : launch_dq_t<bf16, 128>(a, walk_only, s);
+  if (dtype == 0) return launch_dq_bf16(a, d, walk_only, s);
   return d == 64 ? launch_dq_t<float, 64>(a, walk_only, s) : launch_dq_t<float, 128>(a, walk_only, s);
 }
 

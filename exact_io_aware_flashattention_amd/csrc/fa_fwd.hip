@@ -256,7 +256,7 @@ static hipError_t launch_fwd_t(const AttnArgs& a, bool walk_only, hipStream_t s)
 }
 
 hipError_t launch_fwd(const AttnArgs& a, int dtype, int d, bool walk_only, hipStream_t s) {
-  if (dtype == 0) return d == 64 ? launch_fwd_t<bf16, 64>(a, walk_only, s) : launch_fwd_t<bf16, 128>(a, walk_only, s);
+  if (dtype == 0) return launch_fwd_bf16(a, d, walk_only, s);
   return d == 64 ? launch_fwd_t<float, 64>(a, walk_only, s) : launch_fwd_t<float, 128>(a, walk_only, s);
 }
 

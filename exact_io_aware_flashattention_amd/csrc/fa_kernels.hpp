@@ -35,4 +35,9 @@ hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int d, hipStream_t s);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int dtype, int d, bool walk_only, hipStream_t s);
 hipError_t launch_bwd_dq(const AttnArgs& a, int dtype, int d, bool walk_only, hipStream_t s);
 
+// bf16 instances (fa_bf16.hip)
+hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s);
+hipError_t launch_dkdv_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s);
+hipError_t launch_dq_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s);
+
 }  // namespace fa

@@ -1,0 +1,98 @@
+// bf16 tiles staged in LDS by direct buffer-to-LDS loads, and the two ways the
+// matrix-core operands are read back from them (gfx950).
+//
+// Layout: a tile of R rows x D bf16 columns is stored row-major (D * 2 bytes
+// per row) with its 16-byte chunks XOR-swizzled per row: logical chunk c of
+// row r sits at physical chunk c ^ swz(r), swz(r) = 2*(r % 4) + (r / 4) % 2.
+//   * row reads (ds_read_b128, one 16-byte chunk of row l%32 per lane): any
+//     8 consecutive rows put the same logical chunk in 8 different bank
+//     groups;
+//   * transposed reads (ds_read_b64_tr_b16): each 16-lane group reads a
+//     4-row x 16-column block, i.e. 4 rows x 2 chunks; rows 4k..4k+3 map the
+//     chunk pair to 8 different bank groups.
+// Both read kinds are therefore free of LDS bank conflicts.
+//
+// Loads: buffer_load_dword_x4 with the LDS-destination form writes 64 lanes x
+// 16 bytes contiguously at the wave-uniform LDS base, so lane t of a load
+// instruction fetches the global chunk that belongs at physical position t.
+// The buffer resource spans exactly the valid rows of the head, so rows at or
+// beyond N read as zeros without any per-lane branch.
+#pragma once
+
+#include "fa_device.hpp"
+
+namespace fa {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int D>
+struct BTile {
+  static constexpr int ROWB = D * 2;          // bytes per row
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int ROWS_PER_LOAD = 1024 / ROWB;   // rows one wave-wide load fills
+  __device__ static __forceinline__ int off(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
+};
+
+// Buffer resource over rows [0, N) of one head ([N][D] bf16 at base).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, int N, int D) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, N * D * 2, 0x00020000);
+}
+
+// Issue the loads of rows [row0, row0 + R) into the tile at lds (R * D * 2
+// bytes); the wave-wide loads are spread over the work-group's NW waves.
+// Completion: s_waitcnt vmcnt(0) in every wave, then a barrier.
+template <int D, int R, int NW = NT / 64>
+__device__ __forceinline__ void tile_load(__amdgpu_buffer_rsrc_t rsrc, int row0, unsigned char* lds) {
+  using TL = BTile<D>;
+  constexpr int NLOAD = R / TL::ROWS_PER_LOAD;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr_in = lane / TL::CPR;          // row within one load
+  const int p = lane % TL::CPR;              // physical chunk
+#pragma unroll
+  for (int i = wave; i < NLOAD; i += NW) {
+    const int lr = i * TL::ROWS_PER_LOAD + lr_in;
+    const int c = p ^ swz(lr);
+    const int voff = ((row0 + lr) * D + c * 8) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds + i * 1024),
+                                             16, voff, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_loads() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One 16-byte chunk (8 bf16) of row r.
+template <int D>
+__device__ __forceinline__ u32x4 row_chunk(const unsigned char* tile, int r, int c) {
+  return *reinterpret_cast<const u32x4*>(tile + BTile<D>::off(r, c));
+}
+
+// Matrix-core operand for a product whose contraction runs over tile rows:
+// lane l receives column col0 + l % 32 at rows row_base + 4*h + {0..3} and
+// row_base + 8 + 4*h + {0..3} (h = l / 32), i.e. the contraction indices of
+// accumulator registers 8*mm .. 8*mm + 7 when row_base = 16*mm.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int row_base, int col0) {
+  const int lane = threadIdx.x & 63;
+  const int G = lane >> 4, u = lane & 15, h = lane >> 5;
+  const int col = col0 + 16 * (G & 1) + 4 * (u & 3);
+  const int c = col >> 3, within = (col & 7) * 2;
+  const int r1 = row_base + 4 * h + (u >> 2);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(tile + BTile<D>::off(r1, c) + within));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(tile + BTile<D>::off(r1 + 8, c) + within));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// acc += A x B on the 32x32x16 bf16 matrix core.
+__device__ __forceinline__ void mma(f32x16& acc, bf16x8 a, bf16x8 b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+}  // namespace fa

@@ -4,8 +4,8 @@
 //     block_mask[i][j] != 0  and  (not causal or j <= i)  and  128*j < kv_len[b]
 // -- a cell that fails the causal or padding test holds only -inf scores and
 // is skipped exactly like a zero mask cell.  Visited cells are walked in
-// ascending order, each split into two 64-wide tiles; a trailing tile that
-// lies wholly past the valid range is dropped.
+// ascending order, each split into 64- or 32-wide tiles; trailing tiles that
+// lie wholly past the valid range are dropped.
 #pragma once
 
 #include "fa_device.hpp"
@@ -16,12 +16,26 @@ namespace fa {
 struct Walk {
   int base;          // first cell index along the walked direction
   int ncells;        // visited cells
-  int ntiles;        // 64-wide tiles to process
+  int ntiles;        // tiles to process
+  int tsh;           // log2 of the tile width (32 or 64)
   const int* list;   // LDS list of visited cell offsets (block-sparse), or null
 
   __device__ __forceinline__ int cell(int c) const { return base + (list ? list[c] : c); }
-  __device__ __forceinline__ int tile_start(int it) const { return cell(it >> 1) * CELL + (it & 1) * 64; }
-  __device__ __forceinline__ bool first_of_cell(int it) const { return (it & 1) == 0; }
+  __device__ __forceinline__ int tile_start(int it) const {
+    const int per = 7 - tsh;   // log2(tiles per cell)
+    return cell(it >> per) * CELL + ((it & ((1 << per) - 1)) << tsh);
+  }
+  __device__ __forceinline__ bool first_of_cell(int it) const { return (it & ((1 << (7 - tsh)) - 1)) == 0; }
+  // Tiles of the last visited cell that start at or past `limit` are dropped.
+  __device__ __forceinline__ void finish(int limit) {
+    const int per = 7 - tsh;
+    ntiles = ncells << per;
+    if (ncells > 0) {
+      const int rest = limit - cell(ncells - 1) * CELL;   // > 0 for every visited cell
+      const int valid = min(1 << per, (rest + (1 << tsh) - 1) >> tsh);
+      ntiles -= (1 << per) - valid;
+    }
+  }
 };
 
 __device__ __forceinline__ int clamp_kv_len(const AttnArgs& a, int b) {
@@ -32,9 +46,11 @@ __device__ __forceinline__ int clamp_kv_len(const AttnArgs& a, int b) {
 
 // Row walk: key tiles for query cell qi (forward and dQ kernels).  kv_end is
 // the first key position past every allowed key of the cell's rows.
-__device__ inline Walk row_walk(const AttnArgs& a, int qi, int kv_end, int T, int* list, int* scratch4) {
+__device__ inline Walk row_walk(const AttnArgs& a, int qi, int kv_end, int T, int* list, int* scratch4,
+                                int tsh = 6) {
   Walk w;
   w.base = 0;
+  w.tsh = tsh;
   const int jlim = (kv_end + CELL - 1) / CELL;
   if (a.mask) {
     const uint8_t* row = a.mask + (size_t)qi * T;
@@ -44,15 +60,16 @@ __device__ inline Walk row_walk(const AttnArgs& a, int qi, int kv_end, int T, in
     w.ncells = jlim;
     w.list = nullptr;
   }
-  w.ntiles = 2 * w.ncells;
-  if (w.ncells > 0 && w.cell(w.ncells - 1) * CELL + 64 >= kv_end) w.ntiles -= 1;
+  w.finish(kv_end);
   return w;
 }
 
 // Column walk: query tiles for key cell kj (dK/dV kernel).
-__device__ inline Walk col_walk(const AttnArgs& a, int kj, int kvl, int T, int* list, int* scratch4) {
+__device__ inline Walk col_walk(const AttnArgs& a, int kj, int kvl, int T, int* list, int* scratch4,
+                                int tsh = 6) {
   Walk w;
   w.base = a.causal ? kj : 0;
+  w.tsh = tsh;
   w.list = nullptr;
   w.ncells = 0;
   const bool any_key = kj * CELL < kvl;
@@ -67,8 +84,7 @@ __device__ inline Walk col_walk(const AttnArgs& a, int kj, int kvl, int T, int* 
   } else {
     w.ncells = any_key ? count : 0;
   }
-  w.ntiles = 2 * w.ncells;
-  if (w.ncells > 0 && w.cell(w.ncells - 1) * CELL + 64 >= a.N) w.ntiles -= 1;
+  w.finish(a.N);
   return w;
 }
 
