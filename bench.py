@@ -100,6 +100,21 @@ def run_gpu_bench(w, steps, warmup, inp):
     return total_ms / steps, per, wall, (B, H, N, d)
 
 
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration():
+    """One device-to-device copy of COPY_BYTES: read COPY_BYTES, write COPY_BYTES.
+    Its FETCH_SIZE / WRITE_SIZE readings scale the counters of the attention
+    kernels to bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline(w, inp, heads=2):
     """fp64 oracle fwd + bwd on the first `heads` heads of the workload (all rows, all keys)."""
     import numpy as np
@@ -119,13 +134,89 @@ def cpu_baseline(w, inp, heads=2):
             "seconds": round(dt, 2)}
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "long_context_hbm_traffic.txt")
+KERNEL_SYMBOL = {"fwd": "fwd_bf16_kernel<128, false>", "dkdv": "dkdv_bf16_kernel<128, false>",
+                 "dq": "dq_bf16_kernel<128, false>", "pre": "bwd_pre_kernel"}
+
+
+def kernel_source_hash():
+    """SHA-256 over the HIP sources; counter readings are only reported while it matches."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_io_aware_flashattention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, or {} when the
+    kernels changed after the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash():
+        return {}
+    return {k[len("bytes_"):]: float(v) for k, v in kv.items() if k.startswith("bytes_")}
+
+
+def summarize_counters(fetch_csv, write_csv, command):
+    """Write the per-kernel HBM traffic summary from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch).  Each counter is scaled by its
+    reading for the plain copy of COPY_BYTES made by --copy-calibration."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copy_name = next(n for n in fetch if "copyBuffer" in n)
+    f_scale = (COPY_BYTES / 1024) / max(fetch[copy_name])
+    w_scale = (COPY_BYTES / 1024) / max(write[copy_name])
+    lines = ["# HBM traffic per launch, long-context workload (B=1 H=16 N=16384 d=128 bf16 causal)",
+             f"# command: {command}",
+             f"# calibration: a {COPY_BYTES >> 20} MiB device copy reads FETCH_SIZE {max(fetch[copy_name]):.1f} KiB "
+             f"(scale {f_scale:.4f}) and WRITE_SIZE {max(write[copy_name]):.1f} KiB (scale {w_scale:.4f})",
+             f"source_hash = {kernel_source_hash()}",
+             f"fetch_scale = {f_scale:.6f}", f"write_scale = {w_scale:.6f}"]
+    for key, sym in KERNEL_SYMBOL.items():
+        fn = [n for n in fetch if sym in n or (key == "pre" and "bwd_pre" in n)]
+        wn = [n for n in write if sym in n or (key == "pre" and "bwd_pre" in n)]
+        if not fn or not wn:
+            continue
+        fb = statistics.median(fetch[fn[0]]) * 1024 * f_scale
+        wb = statistics.median(write[wn[0]]) * 1024 * w_scale
+        lines += [f"fetch_{key} = {fb:.0f}", f"write_{key} = {wb:.0f}", f"bytes_{key} = {fb + wb:.0f}"]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before the steps, run one plain device copy of COPY_BYTES (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="write profiles/long_context_hbm_traffic.txt from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the attention hot path here is "
               f"single-GPU and has no multi-GPU mode.", file=sys.stderr)
@@ -134,6 +225,8 @@ def main():
     from workloads import WORKLOADS, digest, make_inputs
     w = WORKLOADS[4]
     inp = make_inputs(w)
+    if args.copy_calibration:
+        copy_calibration()
     step_ms, per, wall, (B, H, N, d) = run_gpu_bench(w, args.steps, args.warmup, inp)
     F = flops_fwd(B, H, N, d, w.causal)
     value = 3.5 * F / (step_ms * 1e-3) / 1e12
@@ -141,8 +234,10 @@ def main():
     dom = max(("fwd", "dkdv", "dq"), key=lambda n: per[n])
     ach = kernel_flops(dom, B, H, N, d, w.causal) / (per[dom] * 1e-3) / 1e12
     fwd_ach = kernel_flops("fwd", B, H, N, d, w.causal) / (per["fwd"] * 1e-3) / 1e12
+    traffic = read_traffic()
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic.get(dom)}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),

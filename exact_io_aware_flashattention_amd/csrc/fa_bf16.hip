@@ -53,7 +53,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int bh = L / T_cells, tq = L - bh * T_cells;
   const int qi = a.causal ? T_cells - 1 - tq : tq;   // heaviest causal rows first
   const int b = bh / a.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
 
   const int kvl = clamp_kv_len(a, b);
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int L = xcd_logical_id(blockIdx.x, gridDim.x);
   const int bh = L / T_cells, kj = L - bh * T_cells;
   const int b = bh / a.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
   const int kvl = clamp_kv_len(a, b);
   const Walk walk = col_walk(a, kj, kvl, T_cells, cell_list, scratch4, C::TSH);
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int bh = L / T_cells, tq = L - bh * T_cells;
   const int qi = a.causal ? T_cells - 1 - tq : tq;
   const int b = bh / a.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
   const int kvl = clamp_kv_len(a, b);
   const int q_lo = qi * CELL, q_hi = min(q_lo + CELL, N);

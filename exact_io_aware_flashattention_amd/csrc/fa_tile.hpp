@@ -3,14 +3,17 @@
 //
 // Layout: a tile of R rows x D bf16 columns is stored row-major (D * 2 bytes
 // per row) with its 16-byte chunks XOR-swizzled per row: logical chunk c of
-// row r sits at physical chunk c ^ swz(r), swz(r) = 2*(r % 4) + (r / 4) % 2.
-//   * row reads (ds_read_b128, one 16-byte chunk of row l%32 per lane): any
-//     8 consecutive rows put the same logical chunk in 8 different bank
-//     groups;
-//   * transposed reads (ds_read_b64_tr_b16): each 16-lane group reads a
-//     4-row x 16-column block, i.e. 4 rows x 2 chunks; rows 4k..4k+3 map the
-//     chunk pair to 8 different bank groups.
-// Both read kinds are therefore free of LDS bank conflicts.
+// row r sits at physical chunk c ^ swz(r).  The LDS has 64 four-byte banks
+// (256 bytes per bank line), so a 256-byte row covers every bank once and a
+// 128-byte row half of them.  The two read kinds and what they need:
+//   * row reads (ds_read_b128, lane l reads one chunk of row l % 32): served
+//     16 lanes per cycle, i.e. 16 consecutive rows at the same logical chunk
+//     must land on 16 different chunk positions of the bank line;
+//   * transposed reads (ds_read_b64_tr_b16): served 32 lanes per cycle, i.e.
+//     4 consecutive rows (4k .. 4k+3) x 4 consecutive chunks.
+// d = 128: swz(r) = 4 (r % 4) + (r / 4) % 4;  d = 64: swz(r) = 4 ((r / 2) % 2)
+// + (r / 4) % 4.  Both satisfy both conditions (checked with the LDS bank
+// conflict counter: 4 cycles per row read, 2 per transposed read).
 //
 // Loads: buffer_load_dword_x4 with the LDS-destination form writes 64 lanes x
 // 16 bytes contiguously at the wave-uniform LDS base, so lane t of a load
@@ -25,15 +28,19 @@ namespace fa {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
 template <int D>
 struct BTile {
   static constexpr int ROWB = D * 2;          // bytes per row
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 1024 / ROWB;   // rows one wave-wide load fills
+  __device__ static __forceinline__ int swz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
   __device__ static __forceinline__ int off(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
 };
+
+// Index of the calling wave within the work-group, as a scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Buffer resource over rows [0, N) of one head ([N][D] bf16 at base).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, int N, int D) {
@@ -47,13 +54,15 @@ template <int D, int R, int NW = NT / 64>
 __device__ __forceinline__ void tile_load(__amdgpu_buffer_rsrc_t rsrc, int row0, unsigned char* lds) {
   using TL = BTile<D>;
   constexpr int NLOAD = R / TL::ROWS_PER_LOAD;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  static_assert(NLOAD % NW == 0, "wave-wide loads must divide evenly over the waves");
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int lr_in = lane / TL::CPR;          // row within one load
   const int p = lane % TL::CPR;              // physical chunk
 #pragma unroll
-  for (int i = wave; i < NLOAD; i += NW) {
+  for (int j = 0; j < NLOAD / NW; ++j) {
+    const int i = j * NW + wave;
     const int lr = i * TL::ROWS_PER_LOAD + lr_in;
-    const int c = p ^ swz(lr);
+    const int c = p ^ TL::swz(lr);
     const int voff = ((row0 + lr) * D + c * 8) * 2;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds + i * 1024),
                                              16, voff, 0, 0, 0);
