@@ -15,13 +15,14 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bf16.hip"]
 ARCH = "gfx950"
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wno-unused-command-line-argument",
+    "-Wno-unused-command-line-argument", f"-I{INCLUDE}",
 ]
 
 

@@ -4,7 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "fa_kernels.hpp"
 
 namespace {

@@ -18,6 +18,8 @@
 #include "fa_tile.hpp"
 #include "fa_walk.hpp"
 
+#include <type_traits>
+
 namespace fa {
 
 // Scores of one 32 x 32 block in accumulator layout: register r of lane l
@@ -33,17 +35,26 @@ __device__ __forceinline__ void zero(f32x16& x) {
 
 template <int D>
 struct FwdB {
-  static constexpr int BC = 64;                 // keys per tile
+  static constexpr int BC = 64;                 // keys per tile (one DMA unit of K or V)
   static constexpr int TILE = BC * D * 2;       // bytes of one K or V tile
-  static constexpr int STAGE = 2 * TILE;
   static constexpr int SSTEPS = D / 16;
   static constexpr int NB = D / 32;
 };
 
+// Forward, software-pipelined over 32-key sub-blocks t = 0, 1, ... of the walk:
+//   A(t): S(t+1) = K(t+1) Q^T on the matrix cores (K fragments read one phase
+//         earlier) while the VALU turns S(t) into P~(t) (exp2, row sum, bf16);
+//         V^T(t) fragments are read from LDS;
+//   B(t): O^T += V^T(t) P~^T(t) on the matrix cores while the VALU masks S(t+1)
+//         and takes its row max; K fragments of t+2 are read.
+// K and V tiles have separate two-deep LDS rings.  Per 64-key tile j there is
+// one barrier and one DMA issue (K of tile j+2, V of tile j+1), so every tile
+// is requested two sub-block steps before it is read.
 template <int D, bool WALK_ONLY>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(AttnArgs a) {
   using C = FwdB<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[WALK_ONLY ? 16 : 2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf[WALK_ONLY ? 16 : 2 * C::TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf[WALK_ONLY ? 16 : 2 * C::TILE];
   __shared__ int cell_list[MAX_T];
   __shared__ int scratch4[4];
 
@@ -69,14 +80,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   } else {
     const size_t head = (size_t)bh * N * D;
     const bf16* Q = reinterpret_cast<const bf16*>(a.q) + head;
-    const bf16* K = reinterpret_cast<const bf16*>(a.k) + head;
-    const bf16* V = reinterpret_cast<const bf16*>(a.v) + head;
     bf16* O = reinterpret_cast<bf16*>(a.out0) + head;
-    const auto rk = head_rsrc(K, N, D), rv = head_rsrc(V, N, D);
+    const auto rk = head_rsrc(reinterpret_cast<const bf16*>(a.k) + head, N, D);
+    const auto rv = head_rsrc(reinterpret_cast<const bf16*>(a.v) + head, N, D);
 
     const int qw0 = q_lo + wave * 32;
     const int myq = qw0 + l32;
-    const bool wave_has_rows = qw0 < N;
+    const int ntiles = walk.ntiles, nsub = 2 * ntiles;
 
     u32x4 qf[C::SSTEPS];
 #pragma unroll
@@ -87,50 +97,51 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     for (int nb = 0; nb < C::NB; ++nb) zero(acc[nb]);
     float m_run = neg_inf(), l_run = 0.f;
 
-    auto issue = [&](int it) {
-      unsigned char* st = smem + (it & 1) * C::STAGE;
-      const int kb0 = walk.tile_start(it);
-      tile_load<D, 64>(rk, kb0, st);
-      tile_load<D, 64>(rv, kb0, st + C::TILE);
+    auto issue_k = [&](int j) { tile_load<D, 64>(rk, walk.tile_start(j), kbuf + (j & 1) * C::TILE); };
+    auto issue_v = [&](int j) { tile_load<D, 64>(rv, walk.tile_start(j), vbuf + (j & 1) * C::TILE); };
+    auto key0 = [&](int t) { return walk.tile_start(t >> 1) + 32 * (t & 1); };
+
+    u32x4 kfrag[C::SSTEPS];          // K rows of one sub-block: row l32, chunk 2 st + h
+    bf16x8 vfrag[C::NB][2];          // V^T operands of one sub-block
+    // Stage and half are compile-time constants so every LDS address is a
+    // per-lane base plus an immediate offset.
+    auto read_k = [&](auto stage, auto half) {
+      const unsigned char* ks = kbuf + decltype(stage)::value * C::TILE;
+#pragma unroll
+      for (int st = 0; st < C::SSTEPS; ++st)
+        kfrag[st] = row_chunk<D>(ks, 32 * decltype(half)::value + l32, 2 * st + h);
     };
-    if (walk.ntiles > 0) issue(0);
-
-    for (int it = 0; it < walk.ntiles; ++it) {
-      wait_loads();
-      __syncthreads();
-      if (it + 1 < walk.ntiles) issue(it + 1);
-      const int kb0 = walk.tile_start(it);
-      const unsigned char* Ks = smem + (it & 1) * C::STAGE;
-      const unsigned char* Vs = Ks + C::TILE;
-      if (!wave_has_rows || (a.causal && kb0 > qw0 + 31)) continue;
-
-      // step 1: S^T = K Q^T, two 32-key halves
-      f32x16 s[2];
+    auto read_v = [&](auto stage, auto half) {
+      const unsigned char* vs = vbuf + decltype(stage)::value * C::TILE;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        zero(s[sb]);
+      for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-        for (int st = 0; st < C::SSTEPS; ++st)
-          mma(s[sb], as_bf16x8(row_chunk<D>(Ks, 32 * sb + l32, 2 * st + h)), as_bf16x8(qf[st]));
+        for (int mm = 0; mm < 2; ++mm)
+          vfrag[nb][mm] = tr_operand<D>(vs, 32 * decltype(half)::value + 16 * mm, 32 * nb);
+    };
+    auto scores = [&](f32x16& s) {
+      zero(s);
+#pragma unroll
+      for (int st = 0; st < C::SSTEPS; ++st) mma(s, as_bf16x8(kfrag[st]), as_bf16x8(qf[st]));
+    };
+    // Mask S(t) where needed and return its row max in log2 units (-inf past the walk).
+    auto mask_max = [&](f32x16& s, int t) -> float {
+      if (t >= nsub) return neg_inf();
+      const int k0 = key0(t);
+      if ((k0 + 32 > kvl) || (a.causal && k0 + 31 > qw0)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + acc_row(r, h);
+          if (key >= kvl || (a.causal && key > myq)) s[r] = neg_inf();
+        }
       }
-      if ((kb0 + C::BC > kvl) || (a.causal && kb0 + C::BC - 1 > qw0)) {
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb0 + 32 * sb + acc_row(r, h);
-            if (key >= kvl || (a.causal && key > myq)) s[sb][r] = neg_inf();
-          }
-      }
-      // step 2: tile row max (two lane halves hold disjoint keys of a query)
       float mx = neg_inf();
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-      mx = max_halves(mx);
-      const float mt = mx * a.c;
-      // step 3: refresh the running max only when a score exceeds it by > 2^TAU
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      return max_halves(mx) * a.c;
+    };
+    // Refresh the running max only when a score exceeds it by more than 2^TAU.
+    auto refresh = [&](float mt) {
       if (wave_any(mt > m_run + TAU)) {
         const float m_new = fmaxf(m_run, mt);
         const float alpha = (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -141,25 +152,70 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           for (int r = 0; r < 16; ++r) acc[nb][r] *= alpha;
         m_run = m_new;
       }
+    };
+    // P~(t) from S(t) (in place), its row sum (of the bf16 values the product
+    // uses) into l_run, and O^T += V^T P~^T.
+    auto softmax_pv = [&](f32x16& s) {
       const float mu = (m_run == neg_inf()) ? 0.f : m_run;
-      float ls = 0.f;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -mu));
+      const PackedB pb = pack_bf16(s);
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+      float ls = l_run;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], a.c, -mu));
-          s[sb][r] = p;
-          ls += p;
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const bf16x2 pr = {pb.p[mm][2 * k], pb.p[mm][2 * k + 1]};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ls, false);
         }
-      l_run += ls;
-      // step 4: O^T += V^T P~^T, V^T read transposed from the row-major tile
+      l_run = ls;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const PackedB pb = pack_bf16(s[sb]);
+      for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm) mma(acc[nb], tr_operand<D>(Vs, 32 * sb + 16 * mm, 32 * nb), pb.p[mm]);
+        for (int mm = 0; mm < 2; ++mm) mma(acc[nb], vfrag[nb][mm], pb.p[mm]);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // One 64-key tile j held in LDS stage STG: sub-blocks 2j (in sa) and 2j+1.
+    f32x16 sa, sb;
+    auto tile_step = [&](auto stg, int j) {
+      constexpr int STG = decltype(stg)::value;
+      using S0 = std::integral_constant<int, STG>;
+      using S1 = std::integral_constant<int, 1 - STG>;
+      if (j > 0) wait_loads();     // K of tile j+1 and V of tile j, issued one tile ago
+      __syncthreads();
+      if (j + 2 < ntiles) issue_k(j + 2);
+      if (j + 1 < ntiles) issue_v(j + 1);
+      // sub-block 2j: S(2j+1) while softmax(2j); then O += P~ V
+      read_v(S0(), I0());
+      scores(sb);
+      softmax_pv(sa);
+      read_k(S1(), I0());
+      refresh(mask_max(sb, 2 * j + 1));
+      // sub-block 2j+1: S(2j+2) (next tile) while softmax(2j+1)
+      read_v(S0(), I1());
+      scores(sa);
+      softmax_pv(sb);
+      read_k(S1(), I1());
+      refresh(mask_max(sa, 2 * j + 2));
+    };
+
+    if (nsub > 0) {
+      issue_k(0);
+      issue_v(0);
+      if (ntiles > 1) issue_k(1);
+      wait_loads();
+      __syncthreads();
+      read_k(I0(), I0());
+      scores(sa);
+      read_k(I0(), I1());
+      refresh(mask_max(sa, 0));
+      for (int j = 0; j < ntiles; j += 2) {
+        tile_step(I0(), j);
+        if (j + 1 < ntiles) tile_step(I1(), j + 1);
       }
     }
 

@@ -15,11 +15,18 @@
 // + (r / 4) % 4.  Both satisfy both conditions (checked with the LDS bank
 // conflict counter: 4 cycles per row read, 2 per transposed read).
 //
-// Loads: buffer_load_dword_x4 with the LDS-destination form writes 64 lanes x
-// 16 bytes contiguously at the wave-uniform LDS base, so lane t of a load
+// Loads: buffer_load_dwordx4 with the LDS-destination form writes 64 lanes x
+// 16 bytes contiguously at the LDS address in M0, so lane t of a load
 // instruction fetches the global chunk that belongs at physical position t.
 // The buffer resource spans exactly the valid rows of the head, so rows at or
-// beyond N read as zeros without any per-lane branch.
+// beyond N read as zeros without any per-lane branch.  The load is issued by
+// inline assembly: when the compiler sees an LDS-destination load it cannot
+// tell which LDS bytes it writes, and waits for it (vmcnt(0)) before every
+// later LDS read -- including the reads of the tile being computed, which
+// would serialise the prefetch of the next tile.  Completion is instead
+// established explicitly: s_waitcnt vmcnt(0) in every wave, then a barrier.
+// (Loads the compiler does not know about can only make its own vmcnt waits
+// stricter, since vector-memory loads complete in issue order.)
 #pragma once
 
 #include "fa_device.hpp"
@@ -42,16 +49,29 @@ struct BTile {
 // Index of the calling wave within the work-group, as a scalar.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// Buffer resource over rows [0, N) of one head ([N][D] bf16 at base).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, int N, int D) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, N * D * 2, 0x00020000);
+// Buffer resource (V#) over rows [0, N) of one head ([N][D] bf16 at base):
+// base address, stride 0, num_records = N * D * 2 bytes, raw-buffer format bits.
+__device__ __forceinline__ u32x4 head_rsrc(const void* base, int N, int D) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(N * D * 2)), 0x00020000u};
+}
+
+// One wave-wide 16-byte-per-lane load into LDS at lds (+ 16 * lane).
+__device__ __forceinline__ void dma16(u32x4 rsrc, unsigned char* lds, int voff) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
 }
 
 // Issue the loads of rows [row0, row0 + R) into the tile at lds (R * D * 2
 // bytes); the wave-wide loads are spread over the work-group's NW waves.
 // Completion: s_waitcnt vmcnt(0) in every wave, then a barrier.
 template <int D, int R, int NW = NT / 64>
-__device__ __forceinline__ void tile_load(__amdgpu_buffer_rsrc_t rsrc, int row0, unsigned char* lds) {
+__device__ __forceinline__ void tile_load(u32x4 rsrc, int row0, unsigned char* lds) {
   using TL = BTile<D>;
   constexpr int NLOAD = R / TL::ROWS_PER_LOAD;
   static_assert(NLOAD % NW == 0, "wave-wide loads must divide evenly over the waves");
@@ -64,8 +84,7 @@ __device__ __forceinline__ void tile_load(__amdgpu_buffer_rsrc_t rsrc, int row0,
     const int lr = i * TL::ROWS_PER_LOAD + lr_in;
     const int c = p ^ TL::swz(lr);
     const int voff = ((row0 + lr) * D + c * 8) * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(lds + i * 1024),
-                                             16, voff, 0, 0, 0);
+    dma16(rsrc, lds + i * 1024, voff);
   }
 }
 
