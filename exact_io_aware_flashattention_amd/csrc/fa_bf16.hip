@@ -153,24 +153,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         m_run = m_new;
       }
     };
-    // P~(t) from S(t) (in place), its row sum (of the bf16 values the product
-    // uses) into l_run, and O^T += V^T P~^T.
+    // P~(t) from S(t) (in place), its row sum into l_run, and O^T += V^T P~^T.
+    // (The row sum stays in fp32 VALU adds: v_dot2 on the packed bf16 values
+    // would halve the instruction count but does not co-execute with the
+    // matrix core.)
     auto softmax_pv = [&](f32x16& s) {
       const float mu = (m_run == neg_inf()) ? 0.f : m_run;
+      float ls = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -mu));
+      for (int r = 0; r < 16; ++r) {
+        s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -mu));
+        ls += s[r];
+      }
+      l_run += ls;
       const PackedB pb = pack_bf16(s);
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      const bf16x2 one = {(bf16)1.f, (bf16)1.f};
-      float ls = l_run;
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const bf16x2 pr = {pb.p[mm][2 * k], pb.p[mm][2 * k + 1]};
-          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ls, false);
-        }
-      l_run = ls;
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll

@@ -3,12 +3,8 @@ library through its C ABI binding, and compare against the fp64 oracle.
 
 Tolerances (stated for the hot path of exact attention):
   float32 inputs: max |dO| <= 1e-5, max |dlse| <= 1e-5, gradients max|d|/max|g| <= 1e-5
-  bf16 inputs:    max |dO| <= 1e-2 and mean |dO| <= 1e-3,
-                  gradients max|d| / max|g_oracle| <= 5e-2 per tensor,
-                  max |dlse| <= 2e-3: the bf16 kernels normalise by the sum of the
-                  bf16-rounded probabilities that also feed the P V product, so l
-                  carries a relative error of at most 2^-9 and lse = m + ln l at most
-                  ln(1 + 2^-9) = 1.95e-3.
+  bf16 inputs:    max |dO| <= 1e-2 and mean |dO| <= 1e-3, max |dlse| <= 1e-3,
+                  gradients max|d| / max|g_oracle| <= 5e-2 per tensor
 """
 import sys
 
@@ -16,7 +12,7 @@ import numpy as np
 
 TOL = {
     "f32": dict(o_max=1e-5, o_mean=1e-5, lse=1e-5, grad=1e-5),
-    "bf16": dict(o_max=1e-2, o_mean=1e-3, lse=2e-3, grad=5e-2),
+    "bf16": dict(o_max=1e-2, o_mean=1e-3, lse=1e-3, grad=5e-2),
 }
 
 
