@@ -21,8 +21,8 @@ FA_BF16, FA_F32 = 0, 1
 WALK_FWD, WALK_DKDV, WALK_DQ = 0, 1, 2
 CELL = 128
 
-EXPORTS = ("fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv",
-           "fa_bwd_dq", "fa_debug_visits", "fa_status_str")
+EXPORTS = ("fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd_dkdv_workspace_bytes", "fa_bwd", "fa_bwd_preprocess",
+           "fa_bwd_dkdv", "fa_bwd_dq", "fa_debug_visits", "fa_status_str")
 
 
 class FAError(RuntimeError):
@@ -50,12 +50,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     sig = {
         "fa_fwd": [P, P, P, P, P, I, I, I, I, F, I, P, P, I, P],
-        "fa_bwd_workspace_bytes": [I, I, I, I, I],
+        "fa_bwd_workspace_bytes": [I, I, I, I, I, I],
+        "fa_bwd_dkdv_workspace_bytes": [I, I, I, I],
         "fa_bwd": [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, P, S, P],
         "fa_bwd_preprocess": [P, P, P, I, I, I, I, I, P],
-        "fa_bwd_dkdv": [P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, P],
+        "fa_bwd_dkdv": [P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, P, S, P],
         "fa_bwd_dq": [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, P],
-        "fa_debug_visits": [I, I, I, I, I, I, P, P, I, P, P],
+        "fa_debug_visits": [I, I, I, I, I, I, P, P, I, P, P, S, P],
         "fa_status_str": [I],
     }
     for name, args in sig.items():
@@ -63,6 +64,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.argtypes = args
         fn.restype = ctypes.c_int
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_dkdv_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_str.restype = ctypes.c_char_p
     _lib = lib
     return lib
@@ -143,8 +145,21 @@ def fa_fwd(q, k, v, o=None, lse=None, *, scale=None, causal=False, block_mask=No
     return o, lse
 
 
-def fa_bwd_workspace_bytes(B, H, N, d, dtype=FA_BF16) -> int:
-    return int(load_library().fa_bwd_workspace_bytes(B, H, N, d, dtype))
+def fa_bwd_workspace_bytes(B, H, N, d, dtype=FA_BF16, has_block_mask=False) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, H, N, d, dtype, int(bool(has_block_mask))))
+
+
+def fa_bwd_dkdv_workspace_bytes(N, d, dtype=FA_BF16, has_block_mask=False) -> int:
+    return int(load_library().fa_bwd_dkdv_workspace_bytes(N, d, dtype, int(bool(has_block_mask))))
+
+
+def _workspace(workspace, need, device):
+    import torch
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace is None:
+        return None, 0
+    return workspace, workspace.numel() * workspace.element_size()
 
 
 def fa_bwd(q, k, v, o, dO, lse, dq=None, dk=None, dv=None, *, scale=None, causal=False, block_mask=None,
@@ -155,14 +170,13 @@ def fa_bwd(q, k, v, o, dO, lse, dq=None, dk=None, dv=None, *, scale=None, causal
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = fa_bwd_workspace_bytes(B, H, N, d, _dtype_code(q))
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    need = fa_bwd_workspace_bytes(B, H, N, d, _dtype_code(q), block_mask is not None)
+    workspace, ws_bytes = _workspace(workspace, max(need, 256), q.device)
     _check_like(q, q, k, v, o, dO, lse, dq, dk, dv, workspace, block_mask, kv_len)
     mb, kl = _mask_args(block_mask, kv_len)
     _call("fa_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
           B, H, N, d, _scale(scale, d), int(bool(causal)), mb, kl, _dtype_code(q), _ptr(workspace),
-          workspace.numel() * workspace.element_size(), _stream(stream))
+          ws_bytes, _stream(stream))
     return dq, dk, dv
 
 
@@ -177,15 +191,18 @@ def fa_bwd_preprocess(o, dO, delta=None, *, stream=None):
 
 
 def fa_bwd_dkdv(q, k, v, dO, lse, delta, dk=None, dv=None, *, scale=None, causal=False, block_mask=None,
-                kv_len=None, stream=None):
+                kv_len=None, workspace=None, stream=None):
     import torch
     B, H, N, d = _shape(q)
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    _check_like(q, q, k, v, dO, lse, delta, dk, dv, block_mask, kv_len)
+    need = fa_bwd_dkdv_workspace_bytes(N, d, _dtype_code(q), block_mask is not None)
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
+    _check_like(q, q, k, v, dO, lse, delta, dk, dv, workspace, block_mask, kv_len)
     mb, kl = _mask_args(block_mask, kv_len)
     _call("fa_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
-          B, H, N, d, _scale(scale, d), int(bool(causal)), mb, kl, _dtype_code(q), _stream(stream))
+          B, H, N, d, _scale(scale, d), int(bool(causal)), mb, kl, _dtype_code(q), _ptr(workspace), ws_bytes,
+          _stream(stream))
     return dk, dv
 
 
@@ -202,13 +219,15 @@ def fa_bwd_dq(q, k, v, dO, lse, delta, dq=None, *, scale=None, causal=False, blo
 
 
 def fa_debug_visits(which, B, H, N, d, *, causal=False, block_mask=None, kv_len=None, dtype=FA_BF16,
-                    device="cuda", stream=None):
+                    device="cuda", workspace=None, stream=None):
     """Visit counters [B, T, T] (uint32 stored in int32) of the forward (0),
     dK/dV (1) or dQ (2) tile walk."""
     import torch
     T = -(-N // CELL)
     counts = torch.zeros((B, T, T), dtype=torch.int32, device=device)
+    need = fa_bwd_dkdv_workspace_bytes(N, d, dtype, block_mask is not None) if which == WALK_DKDV else 0
+    workspace, ws_bytes = _workspace(workspace, need, device)
     mb, kl = _mask_args(block_mask, kv_len)
     _call("fa_debug_visits", int(which), B, H, N, d, int(bool(causal)), mb, kl, int(dtype), _ptr(counts),
-          _stream(stream))
+          _ptr(workspace), ws_bytes, _stream(stream))
     return counts

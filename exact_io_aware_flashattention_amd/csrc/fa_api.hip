@@ -28,9 +28,11 @@ int check_shape(const Shape& s, const uint8_t* block_mask, bool* empty) {
   if (*empty) return FA_OK;
   const long long T = (s.N + kCell - 1) / kCell;
   if (block_mask && T > kMaxCells) return FA_ERR_SHAPE;
-  // work-group counts and row indices stay within int
-  if (T * s.H * s.B > 0x7fffffffLL) return FA_ERR_SHAPE;
-  if ((long long)s.B * s.H * s.N > 0x7fffffffLL) return FA_ERR_SHAPE;
+  // A launch covers fewer than 2^32 work-items: the attention kernels run
+  // T*H*B work-groups of 256 (plus the split items of dK/dV), the backward
+  // preprocess at most 32 threads per row.  In-head offsets stay within int.
+  if (T * s.H * s.B + fa::SPLIT_MAX_ITEMS >= (1LL << 32) / fa::NT_HOST) return FA_ERR_SHAPE;
+  if ((long long)s.B * s.H * s.N >= (1LL << 32) / 32 - fa::NT_HOST) return FA_ERR_SHAPE;
   if ((long long)s.N * s.d > 0x7fffffffLL) return FA_ERR_SHAPE;
   return FA_OK;
 }
@@ -75,6 +77,22 @@ fa::AttnArgs make_args(const Shape& s, float scale, int causal, const uint8_t* b
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+size_t delta_bytes(int B, int H, int N) {
+  const size_t bytes = (size_t)B * H * N * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+// The dK/dV split workspace, when this call needs one.
+int split_workspace(fa::AttnArgs& a, const Shape& s, void* ws, size_t ws_bytes) {
+  const size_t need = s.dtype == FA_BF16 && a.mask ? fa::split_ws_bytes(s.N, s.d) : 0;
+  if (need == 0) return FA_OK;
+  if (!ws) return FA_ERR_NULL;
+  if (!aligned(ws, 16)) return FA_ERR_ALIGN;
+  if (ws_bytes < need) return FA_ERR_WORKSPACE;
+  a.split = fa::split_ws_carve(ws, s.N, s.d);
+  return FA_OK;
+}
+
 #define FA_TRY(expr)            \
   do {                          \
     const int _st = (expr);     \
@@ -99,12 +117,14 @@ const char* fa_status_str(int status) {
   }
 }
 
-size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
-  (void)d;
-  (void)dtype;
+size_t fa_bwd_dkdv_workspace_bytes(int N, int d, int dtype, int has_block_mask) {
+  if (N <= 0 || (d != 64 && d != 128) || dtype != FA_BF16 || !has_block_mask) return 0;
+  return fa::split_ws_bytes(N, d);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int has_block_mask) {
   if (B <= 0 || H <= 0 || N <= 0) return 0;
-  const size_t bytes = (size_t)B * H * N * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+  return delta_bytes(B, H, N) + fa_bwd_dkdv_workspace_bytes(N, d, dtype, has_block_mask);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
@@ -144,7 +164,8 @@ int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H,
 
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                 const float* delta, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
-                const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* stream) {
+                const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
   const Shape s{B, H, N, d, dtype};
   bool empty = false;
   FA_TRY(check_shape(s, block_mask, &empty));
@@ -162,6 +183,7 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, con
   a.delta = const_cast<float*>(delta);
   a.out0 = dk;
   a.out1 = dv;
+  FA_TRY(split_workspace(a, s, workspace, workspace_bytes));
   return hip_status(fa::launch_bwd_dkdv(a, dtype, d, false, static_cast<hipStream_t>(stream)));
 }
 
@@ -201,16 +223,19 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   FA_TRY(check_scale(scale));
   if (!workspace) return FA_ERR_NULL;
   if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
-  if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
+  if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d, dtype, block_mask != nullptr))
+    return FA_ERR_WORKSPACE;
   float* delta = static_cast<float*>(workspace);
+  const size_t db = delta_bytes(B, H, N);
   FA_TRY(fa_bwd_preprocess(o, dO, delta, B, H, N, d, dtype, stream));
   FA_TRY(fa_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, B, H, N, d, scale, causal, block_mask, kv_len, dtype,
-                     stream));
+                     static_cast<unsigned char*>(workspace) + db, workspace_bytes - db, stream));
   return fa_bwd_dq(q, k, v, dO, lse, delta, dq, B, H, N, d, scale, causal, block_mask, kv_len, dtype, stream);
 }
 
 int fa_debug_visits(int which, int B, int H, int N, int d, int causal, const uint8_t* block_mask,
-                    const int32_t* kv_len, int dtype, uint32_t* counts, void* stream) {
+                    const int32_t* kv_len, int dtype, uint32_t* counts, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   const Shape s{B, H, N, d, dtype};
   bool empty = false;
   if (which < fa::WALK_FWD || which > fa::WALK_DQ) return FA_ERR_ARG;
@@ -221,6 +246,7 @@ int fa_debug_visits(int which, int B, int H, int N, int d, int causal, const uin
   FA_TRY(check_masks(block_mask, kv_len));
   fa::AttnArgs a = make_args(s, 1.f, causal, block_mask, kv_len);
   a.counts = counts;
+  if (which == fa::WALK_DKDV) FA_TRY(split_workspace(a, s, workspace, workspace_bytes));
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (which == fa::WALK_FWD)

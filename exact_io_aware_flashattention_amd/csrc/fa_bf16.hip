@@ -244,7 +244,10 @@ struct DkdvB {
   static constexpr int NB = D / 32;
 };
 
-template <int D, bool WALK_ONLY>
+// SPLIT (block mask present): work-groups [0, SPLIT_MAX_ITEMS) take the split
+// items of the plan (a chunk of a long column each; surplus ones exit), the
+// rest take one column each and exit if the column is split.
+template <int D, bool WALK_ONLY, bool SPLIT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_bf16_kernel(AttnArgs a) {
   using C = DkdvB<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[WALK_ONLY ? 16 : C::VRES + 2 * C::STAGE];
@@ -253,13 +256,36 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   const int N = a.N;
   const int T_cells = (N + CELL - 1) / CELL;
-  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int bh = L / T_cells, kj = L - bh * T_cells;
+  const bool split_item = SPLIT && blockIdx.x < (unsigned)SPLIT_MAX_ITEMS;
+  int bh, kj, c0 = 0, ch = 0;   // split item: the chunk's first cell and CH
+  if (split_item) {
+    const int g = blockIdx.x;
+    if (g >= a.split.hdr[0]) return;
+    const int P = a.split.hdr[1];
+    ch = a.split.hdr[2];
+    bh = g / P;
+    const int r = g - bh * P;
+    const int* e = a.split.table + 4 * r;
+    kj = e[0];
+    c0 = (r - e[1]) * ch;
+  } else {
+    const int off = SPLIT ? SPLIT_MAX_ITEMS : 0;
+    const int L = xcd_logical_id(blockIdx.x - off, gridDim.x - off);
+    bh = L / T_cells;
+    kj = L - bh * T_cells;
+  }
   const int b = bh / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
   const int kvl = clamp_kv_len(a, b);
-  const Walk walk = col_walk(a, kj, kvl, T_cells, cell_list, scratch4, C::TSH);
+  int listed = 0;
+  Walk walk = col_walk(a, kj, kvl, T_cells, cell_list, scratch4, C::TSH, &listed);
+  if constexpr (SPLIT) {
+    if (split_item)
+      take_chunk(walk, c0, ch, N);
+    else if (listed > a.split.hdr[2])
+      return;   // the split items of this column cover it
+  }
 
   if constexpr (WALK_ONLY) {
     for (int it = 0; it < walk.ntiles; ++it)
@@ -363,6 +389,56 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
     }
 
+    if constexpr (SPLIT) {
+      if (split_item) {
+        // partial sums of this chunk -> slot [2][D/4][128 keys][4]; lanes of a
+        // half write 512 contiguous bytes per store.  (Item data are read again
+        // here rather than kept live through the main loop.)
+        const int item = blockIdx.x, P = a.split.hdr[1];
+        const int* e = a.split.table + 4 * (item - bh * P);
+        const int first = bh * P + e[1], nchunk = e[2];
+        const int kl = wave * 32 + l32;
+        float* slot = a.split.slots + (size_t)item * (2 * CELL * D);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const size_t o = ((size_t)(8 * nb + 2 * g + h) * CELL + kl) * 4;
+            *reinterpret_cast<f32x4*>(slot + o) =
+                f32x4{dk[nb][4 * g], dk[nb][4 * g + 1], dk[nb][4 * g + 2], dk[nb][4 * g + 3]};
+            *reinterpret_cast<f32x4*>(slot + CELL * D + o) =
+                f32x4{dv[nb][4 * g], dv[nb][4 * g + 1], dv[nb][4 * g + 2], dv[nb][4 * g + 3]};
+          }
+        __threadfence();   // release this thread's partials at device scope
+        __syncthreads();
+        if (tid == 0) scratch4[0] = atomicAdd(a.split.ctr + first, 1u) == (unsigned)(nchunk - 1);
+        __syncthreads();
+        if (!scratch4[0]) return;   // another chunk of the column finishes later
+        __threadfence();   // acquire the other chunks' partials
+        // the last chunk adds all partials of the column in chunk order
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+          zero(dk[nb]);
+          zero(dv[nb]);
+        }
+        for (int c = 0; c < nchunk; ++c) {
+          const float* sl = a.split.slots + (size_t)(first + c) * (2 * CELL * D);
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const size_t o = ((size_t)(8 * nb + 2 * g + h) * CELL + kl) * 4;
+              const f32x4 x = *reinterpret_cast<const f32x4*>(sl + o);
+              const f32x4 y = *reinterpret_cast<const f32x4*>(sl + CELL * D + o);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                dk[nb][4 * g + e] += x[e];
+                dv[nb][4 * g + e] += y[e];
+              }
+            }
+        }
+      }
+    }
     if (myk < N) {
       bf16* dkp = reinterpret_cast<bf16*>(a.out0) + head + (size_t)myk * D;
       bf16* dvp = reinterpret_cast<bf16*>(a.out1) + head + (size_t)myk * D;
@@ -518,8 +594,29 @@ struct Launch;
   }
 
 FA_DEFINE_LAUNCH(launch_fwd_b, fwd_bf16_kernel)
-FA_DEFINE_LAUNCH(launch_dkdv_b, dkdv_bf16_kernel)
 FA_DEFINE_LAUNCH(launch_dq_b, dq_bf16_kernel)
+
+// dK/dV: with a block mask the split plan runs first and SPLIT_MAX_ITEMS
+// work-groups for split items precede the per-column ones.
+template <int D>
+static hipError_t launch_dkdv_b(const AttnArgs& a, bool walk_only, hipStream_t s) {
+  const long long ncol = (long long)((a.N + CELL - 1) / CELL) * a.H * a.B;
+  if (!a.mask) {
+    if (walk_only)
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, true, false>), dim3((unsigned)ncol), dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, false, false>), dim3((unsigned)ncol), dim3(NT), 0, s, a);
+    return hipGetLastError();
+  }
+  const hipError_t e = launch_split_plan(a, s);
+  if (e != hipSuccess) return e;
+  const long long nwg = SPLIT_MAX_ITEMS + ncol;
+  if (walk_only)
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, true, true>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, false, true>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s) {
   return d == 64 ? launch_fwd_b<64>(a, walk_only, s) : launch_fwd_b<128>(a, walk_only, s);

@@ -3,12 +3,35 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace fa {
 
 // Which kernel fa_debug_visits walks.
 enum WalkKind { WALK_FWD = 0, WALK_DKDV = 1, WALK_DQ = 2 };
+
+// Work split of the dK/dV column walks under a block mask.  Without it one
+// key column of the mask that many query cells visit (a global column) is
+// walked by a single work-group while the rest of the chip idles.  A plan
+// fixes a chunk size CH (cells); every column with more than CH visited cells
+// is cut into chunks of CH consecutive cells, each chunk its own work-group
+// ("split item"); each chunk writes its fp32 partial dK/dV into a slot and
+// the last chunk of a column to finish adds the slots in chunk order (so the
+// result does not depend on the finishing order) and stores dK/dV.
+constexpr int NT_HOST = 256;              // threads per attention work-group
+constexpr int SPLIT_TARGET = 512;          // concurrent dK/dV work-groups on the chip
+constexpr int SPLIT_MAX_ITEMS = 2 * SPLIT_TARGET;   // bound on split items, see the plan kernel
+constexpr int SPLIT_MIN_CELLS = 16;        // smallest chunk
+constexpr int SPLIT_COUNT_ROWS = 64;       // mask rows per partial column count
+
+struct SplitWs {
+  int* hdr;          // [0] split items, [1] P = split items per head, [2] CH
+  int* table;        // [P][4]: key cell, first entry of that cell, its chunks, 0
+  unsigned* ctr;     // [items] arrival counters (entry of a column's first chunk)
+  float* slots;      // [items][2][D/4][128][4] fp32 partial dK, dV
+  int* part;         // [ceil(T/64)][T] visited-cell counts per column and row band
+};
 
 struct AttnArgs {
   const void* q;
@@ -27,7 +50,13 @@ struct AttnArgs {
   const uint8_t* mask;  // [T][T] or null
   const int32_t* kv_len;  // [B] or null
   uint32_t* counts;     // visit counters (walk-only instances)
+  SplitWs split;        // dK/dV work split (bf16 with a block mask), else zeros
 };
+
+// Bytes of the dK/dV split workspace for N keys and head dimension d; the
+// offsets of its parts follow the order of SplitWs.
+size_t split_ws_bytes(int N, int d);
+SplitWs split_ws_carve(void* base, int N, int d);
 
 // dtype: 0 = bf16, 1 = f32;  d: 64 or 128.
 hipError_t launch_fwd(const AttnArgs& a, int dtype, int d, bool walk_only, hipStream_t s);
@@ -39,5 +68,7 @@ hipError_t launch_bwd_dq(const AttnArgs& a, int dtype, int d, bool walk_only, hi
 hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s);
 hipError_t launch_dkdv_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s);
 hipError_t launch_dq_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s);
+// Column counts + plan of the dK/dV split (needs a.mask and a.split).
+hipError_t launch_split_plan(const AttnArgs& a, hipStream_t s);
 
 }  // namespace fa

@@ -64,28 +64,37 @@ __device__ inline Walk row_walk(const AttnArgs& a, int qi, int kv_end, int T, in
   return w;
 }
 
-// Column walk: query tiles for key cell kj (dK/dV kernel).
+// Column walk: query tiles for key cell kj (dK/dV kernel).  *listed gets the
+// number of cells the mask and the causal test allow in the column, whether
+// or not the column holds any key below kv_len (the split plan counts the
+// same cells).
 __device__ inline Walk col_walk(const AttnArgs& a, int kj, int kvl, int T, int* list, int* scratch4,
-                                int tsh = 6) {
+                                int tsh = 6, int* listed = nullptr) {
   Walk w;
   w.base = a.causal ? kj : 0;
   w.tsh = tsh;
   w.list = nullptr;
-  w.ncells = 0;
   const bool any_key = kj * CELL < kvl;
   const int count = T - w.base;
+  int n = count;
   if (a.mask) {
     const uint8_t* col = a.mask + kj;
     const int base = w.base;
-    const int n = build_list(any_key ? count : 0, [&](int c) { return col[(size_t)(base + c) * T] != 0; },
-                             list, scratch4);
-    w.ncells = n;
+    n = build_list(count, [&](int c) { return col[(size_t)(base + c) * T] != 0; }, list, scratch4);
     w.list = list;
-  } else {
-    w.ncells = any_key ? count : 0;
   }
+  if (listed) *listed = n;
+  w.ncells = any_key ? n : 0;
   w.finish(a.N);
   return w;
+}
+
+// Restrict a block-sparse walk to its visited cells [c0, c0 + cnt) (one chunk
+// of a split column).
+__device__ inline void take_chunk(Walk& w, int c0, int cnt, int limit) {
+  w.list += c0;
+  w.ncells = max(0, min(w.ncells - c0, cnt));
+  w.finish(limit);
 }
 
 }  // namespace fa

@@ -67,7 +67,7 @@ enum fa_status {
   FA_ERR_SHAPE = 2,     /* negative size, d not 64/128, T > 2048 or too large */
   FA_ERR_DTYPE = 3,     /* dtype not FA_BF16 / FA_F32 */
   FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
-  FA_ERR_WORKSPACE = 5, /* workspace smaller than fa_bwd_workspace_bytes() */
+  FA_ERR_WORKSPACE = 5, /* workspace smaller than the matching *_workspace_bytes() */
   FA_ERR_HIP = 6,       /* a HIP launch failed */
   FA_ERR_ARG = 7        /* scale not finite and > 0, or bad selector */
 };
@@ -88,15 +88,28 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of workspace fa_bwd needs: the float32 row terms
- * delta_i = sum_k dO_ik O_ik, [B,H,N], rounded up to 256.  Linear in N.
+ * delta_i = sum_k dO_ik O_ik, [B,H,N], rounded up to 256, followed by
+ * fa_bwd_dkdv_workspace_bytes(N, d, dtype, has_block_mask) bytes.
+ * has_block_mask: nonzero if the call will pass a block mask.
  */
-size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int has_block_mask);
+
+/*
+ * Bytes of workspace fa_bwd_dkdv needs.  Zero unless dtype is FA_BF16 and a
+ * block mask is passed: then the key columns of the mask that many query
+ * cells visit are split over several work-groups, which need a plan, arrival
+ * counters and float32 partial sums for at most 1024 column chunks
+ * (1024 * 2 * 128 * d * 4 bytes plus about ceil(N/128)^2 / 16 bytes; 64 MiB
+ * at d = 64, 128 MiB at d = 128).  Independent of B and H.
+ */
+size_t fa_bwd_dkdv_workspace_bytes(int N, int d, int dtype, int has_block_mask);
 
 /*
  * Backward pass for the loss gradient dO: writes dq, dk, dv (dtype).  Runs
  * fa_bwd_preprocess, fa_bwd_dkdv and fa_bwd_dq in that order on `stream`,
- * with delta in `workspace` (at least fa_bwd_workspace_bytes bytes, 16-byte
- * aligned).  o and lse must be the outputs of fa_fwd on the same q, k, v,
+ * with delta, then the dk/dv workspace, in `workspace` (at least
+ * fa_bwd_workspace_bytes bytes for the same sizes and mask presence, 16-byte
+ * aligned; its contents need no initialisation and are overwritten).  o and lse must be the outputs of fa_fwd on the same q, k, v,
  * scale and masks.  The pages print no backward equations; the ones used
  * follow from the definition by the chain rule:
  *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta),
@@ -116,12 +129,18 @@ int fa_bwd_preprocess(const void* o, const void* dO, float* delta,
 /*
  * Backward stage 2: dk, dv.  Each work-group owns 128 keys (one mask cell
  * column) and walks the query tiles that visit it, recomputing S and P from
- * q, k and lse.
+ * q, k and lse.  With a block mask (FA_BF16), a column with more visited
+ * cells than a plan's chunk size is split into chunks, one work-group each,
+ * whose float32 partial sums are added in chunk order (the result does not
+ * depend on the order in which they finish).  workspace: at least
+ * fa_bwd_dkdv_workspace_bytes bytes, 16-byte aligned (may be NULL when that
+ * is zero); two calls that share a workspace must not overlap in time.
  */
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
                 const float* lse, const float* delta, void* dk, void* dv,
                 int B, int H, int N, int d, float scale, int causal,
-                const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* stream);
+                const uint8_t* block_mask, const int32_t* kv_len, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward stage 3: dq.  Each work-group owns 128 queries and walks the same
@@ -139,10 +158,12 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
  * zeroed by the caller) for every head h and every visited cell (query cell i,
  * key cell j).  A cell is visited iff block_mask[i][j] != 0, (not causal or
  * j <= i) and 128*j < kv_len[b].  d and dtype select the kernel instance.
+ * workspace: as for fa_bwd_dkdv when which = 1, else unused (may be NULL);
+ * with a split column each chunk counts its own cells.
  */
 int fa_debug_visits(int which, int B, int H, int N, int d, int causal,
                     const uint8_t* block_mask, const int32_t* kv_len, int dtype,
-                    uint32_t* counts, void* stream);
+                    uint32_t* counts, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* fa_status_str(int status);

@@ -40,10 +40,26 @@ def test_status_strings(lib):
 
 
 def test_workspace_is_linear_in_n(lib):
-    w1 = lib.fa_bwd_workspace_bytes(1, 16, 16384, 128, 0)
-    w2 = lib.fa_bwd_workspace_bytes(1, 16, 32768, 128, 0)
+    w1 = lib.fa_bwd_workspace_bytes(1, 16, 16384, 128, 0, 0)
+    w2 = lib.fa_bwd_workspace_bytes(1, 16, 32768, 128, 0, 0)
     assert w1 >= 16 * 16384 * 4 and w2 == 2 * w1
-    assert lib.fa_bwd_workspace_bytes(0, 1, 1, 64, 0) == 0
+    assert lib.fa_bwd_workspace_bytes(0, 1, 1, 64, 0, 0) == 0
+
+
+def test_split_workspace_size(lib):
+    """The dK/dV split workspace: only bf16 with a block mask, bounded slot pool
+    (1024 chunks x 128 keys x d x {dK, dV} x fp32) plus a mask-sized count table."""
+    for d in (64, 128):
+        pool = 1024 * 2 * 128 * d * 4
+        T = 512
+        w = lib.fa_bwd_dkdv_workspace_bytes(T * 128, d, 0, 1)
+        assert pool <= w <= pool + 64 * 1024 + (T // 64) * T * 4 + 1024
+        assert lib.fa_bwd_dkdv_workspace_bytes(T * 128, d, 0, 0) == 0
+        assert lib.fa_bwd_dkdv_workspace_bytes(T * 128, d, 1, 1) == 0      # float32 path: none
+        full = lib.fa_bwd_workspace_bytes(2, 3, T * 128, d, 0, 1)
+        assert full == lib.fa_bwd_workspace_bytes(2, 3, T * 128, d, 0, 0) + w
+        # independent of B and H
+        assert lib.fa_bwd_dkdv_workspace_bytes(T * 128, d, 0, 1) == w
 
 
 FAKE = 1 << 20          # an aligned, never-dereferenced address
@@ -81,20 +97,40 @@ def test_backward_validation(lib):
         return lib.fa_bwd(P, P, P, P, P, P, dq, P, P, 2, 4, 1000, 128, scale, 1, None, None, 0,
                           ws, ws_bytes, None)
 
-    need = lib.fa_bwd_workspace_bytes(2, 4, 1000, 128, 0)
+    need = lib.fa_bwd_workspace_bytes(2, 4, 1000, 128, 0, 0)
     assert bwd(ws_bytes=need - 1) == 5                 # FA_ERR_WORKSPACE
     assert bwd(ws=None) == 1
     assert bwd(dq=None) == 1
     assert bwd(scale=float("inf")) == 7
-    assert lib.fa_bwd_dkdv(P, P, P, P, P, P, P, P, 1, 1, 100, 64, -1.0, 0, None, None, 0, None) == 7
+
+    def bwd_masked(ws_bytes):
+        return lib.fa_bwd(P, P, P, P, P, P, P, P, P, 2, 4, 1000, 128, 0.125, 1, P, None, 0, P, ws_bytes, None)
+
+    # with a block mask the workspace grows by the dK/dV split part
+    need_m = lib.fa_bwd_workspace_bytes(2, 4, 1000, 128, 0, 1)
+    assert need_m > need
+    assert bwd_masked(need) == 5
+    assert bwd_masked(need_m - 1) == 5
+
+    def dkdv(ws, ws_bytes, scale=0.125):
+        return lib.fa_bwd_dkdv(P, P, P, P, P, P, P, P, 1, 1, 300, 64, scale, 0, P, None, 0, ws, ws_bytes, None)
+
+    w = lib.fa_bwd_dkdv_workspace_bytes(300, 64, 0, 1)
+    assert dkdv(None, w) == 1                          # bf16 + mask: FA_ERR_NULL
+    assert dkdv(P + 8, w) == 4                         # FA_ERR_ALIGN
+    assert dkdv(P, w - 1) == 5                         # FA_ERR_WORKSPACE
+    assert dkdv(P, w, scale=-1.0) == 7
     assert lib.fa_bwd_dq(P, P, P, P, None, P, P, 1, 1, 100, 64, 0.1, 0, None, None, 0, None) == 1
     assert lib.fa_bwd_preprocess(P, P, P, 1, 1, 100, 80, 0, None) == 2
 
 
 def test_debug_visits_validation(lib):
-    assert lib.fa_debug_visits(3, 1, 1, 128, 64, 0, None, None, 0, FAKE, None) == 7
-    assert lib.fa_debug_visits(0, 1, 1, 128, 64, 0, None, None, 0, None, None) == 1
-    assert lib.fa_debug_visits(0, 1, 1, 0, 64, 0, None, None, 0, None, None) == 0
+    assert lib.fa_debug_visits(3, 1, 1, 128, 64, 0, None, None, 0, FAKE, None, 0, None) == 7
+    assert lib.fa_debug_visits(0, 1, 1, 128, 64, 0, None, None, 0, None, None, 0, None) == 1
+    assert lib.fa_debug_visits(0, 1, 1, 0, 64, 0, None, None, 0, None, None, 0, None) == 0
+    # the dK/dV walk under a block mask needs the split workspace
+    assert lib.fa_debug_visits(1, 1, 1, 128, 64, 0, FAKE, None, 0, FAKE, None, 0, None) == 1
+    assert lib.fa_debug_visits(1, 1, 1, 128, 64, 0, FAKE, None, 0, FAKE, FAKE, 1, None) == 5
 
 
 def test_library_links_only_hip_runtime():

@@ -131,6 +131,46 @@ def test_deterministic_repeat():
         assert np.array_equal(a[n], b[n]), n
 
 
+def split_mask(T, seed, heavy_col):
+    """Band + one random cell per row + a global column 0 (band_random_mask)
+    plus one more fully set column: two key columns that every query cell
+    visits."""
+    bm = band_random_mask(T, seed, n_random=1)
+    bm[:, heavy_col] = 1
+    return bm
+
+
+SPLIT_CASES = [
+    # B, H, N, d, causal, kv_len
+    (2, 2, 5083, 64, False, None),
+    (1, 2, 5083, 128, True, None),
+    (2, 1, 5083, 64, True, [5083, 1000]),   # b = 1: the set column 20 lies past kv_len
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "B{}H{}N{}d{}{}{}".format(
+    c[0], c[1], c[2], c[3], "c" if c[4] else "", "k" if c[5] else ""))
+def test_split_key_columns(case):
+    """Block-sparse dK/dV with key columns long enough to be split over several
+    work-groups (a column is split when it holds more visited cells than the
+    chunk, max(16, ceil(visited cells of all heads / 512)) = 16 here, and the
+    set columns hold 20-40).  Element-wise against the dense oracle, and the
+    order-fixed reduction of the partial sums makes a repeat bit-identical."""
+    B, H, N, d, causal, kv = case
+    T = -(-N // 128)
+    bm = split_mask(T, 2100 + d, 20)
+    per_head = bm[np.arange(T)[:, None] >= np.arange(T)[None, :]].sum() if causal else bm.sum()
+    chunk = max(16, -(-int(B * H * per_head) // 512))
+    assert chunk == 16 and (bm[:, 0].sum() > chunk)
+    inp = small_inputs(B, H, N, d, "bf16", causal, kv=kv, mask=bm, seed=N + d)
+    out = check_full(inp, f"split {case}")
+    again = run_gpu(inp)
+    for n in ("dk", "dv"):
+        assert np.array_equal(out[n], again[n]), n
+    if kv is not None:
+        assert np.all(out["dk"][1, :, kv[1]:] == 0) and np.all(out["dv"][1, :, kv[1]:] == 0)
+
+
 def test_empty_problem_is_a_no_op():
     import torch
 

@@ -40,6 +40,9 @@ CASES = [
     (1, 2, 1024, 64, True, "band", None),
     (3, 1, 777, 128, True, "bern", "rand"),
     (2, 2, 2048, 64, False, "bern", [0, 2048]),
+    # key columns 0 and 20 visited by every query cell: the dK/dV walk splits them
+    (2, 2, 5083, 64, False, "split", [5083, 1000]),
+    (1, 2, 5083, 128, True, "split", None),
 ]
 
 
@@ -53,6 +56,9 @@ def test_walk_matches_expected(case):
     elif mask == "bern":
         rng = np.random.Generator(np.random.PCG64(12))
         bm = (rng.random((T, T)) < 0.3).astype(np.uint8)
+    elif mask == "split":
+        bm = band_random_mask(T, 14, n_random=1)
+        bm[:, 20] = 1
     if kv == "rand":
         kv = draw_kv_len(B, 1, N, 13)
     run_walks(B, H, N, d, causal, bm, kv)
