@@ -26,6 +26,14 @@ namespace fa {
 // belongs to the key/query pair (8*(r/4) + 4*h + r%4, l % 32).
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// Max of the 16 accumulator entries of a lane as a depth-3 tree of v_max3.
+__device__ __forceinline__ float max16(const f32x16& s) {
+  const float m0 = fmaxf(fmaxf(s[0], s[1]), s[2]), m1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
+  const float m2 = fmaxf(fmaxf(s[6], s[7]), s[8]), m3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
+  const float m4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
+  return fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), s[15]));
+}
+
 __device__ __forceinline__ void zero(f32x16& x) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) x[r] = 0.f;
@@ -81,8 +89,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const size_t head = (size_t)bh * N * D;
     const bf16* Q = reinterpret_cast<const bf16*>(a.q) + head;
     bf16* O = reinterpret_cast<bf16*>(a.out0) + head;
-    const auto rk = head_rsrc(reinterpret_cast<const bf16*>(a.k) + head, N, D);
-    const auto rv = head_rsrc(reinterpret_cast<const bf16*>(a.v) + head, N, D);
+    const bf16* Kh = reinterpret_cast<const bf16*>(a.k) + head;
+    const bf16* Vh = reinterpret_cast<const bf16*>(a.v) + head;
+    const TileDma<D, 64> dma;
 
     const int qw0 = q_lo + wave * 32;
     const int myq = qw0 + l32;
@@ -95,10 +104,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     f32x16 acc[C::NB];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) zero(acc[nb]);
-    float m_run = neg_inf(), l_run = 0.f;
+    // Running max m_run (log2 units), kept with the two values the tile loop
+    // uses: neg_mu = -m_run (0 while m_run = -inf) enters every exponent, and
+    // thr = (m_run + TAU) / c is the raw-score level above which the running
+    // max must move (-inf while m_run = -inf).
+    float m_run = neg_inf(), l_run = 0.f, neg_mu = 0.f, thr = neg_inf();
+    const float inv_c = 1.f / a.c;
 
-    auto issue_k = [&](int j) { tile_load<D, 64>(rk, walk.tile_start(j), kbuf + (j & 1) * C::TILE); };
-    auto issue_v = [&](int j) { tile_load<D, 64>(rv, walk.tile_start(j), vbuf + (j & 1) * C::TILE); };
+    auto issue_k = [&](int j) { dma.load(Kh, N, walk.tile_start(j), kbuf + (j & 1) * C::TILE); };
+    auto issue_v = [&](int j) { dma.load(Vh, N, walk.tile_start(j), vbuf + (j & 1) * C::TILE); };
     auto key0 = [&](int t) { return walk.tile_start(t >> 1) + 32 * (t & 1); };
 
     u32x4 kfrag[C::SSTEPS];          // K rows of one sub-block: row l32, chunk 2 st + h
@@ -124,26 +138,29 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
       for (int st = 0; st < C::SSTEPS; ++st) mma(s, as_bf16x8(kfrag[st]), as_bf16x8(qf[st]));
     };
-    // Mask S(t) where needed and return its row max in log2 units (-inf past the walk).
+    // Mask S(t) where needed and return the lane's raw max over its 16
+    // entries (-inf past the walk).
+    // Register r holds key k0 + acc_row(r, h), which is masked iff it is at or
+    // past kv_len or (causal) past the lane's query: acc_row(r, 0) >= lim.
     auto mask_max = [&](f32x16& s, int t) -> float {
       if (t >= nsub) return neg_inf();
       const int k0 = key0(t);
       if ((k0 + 32 > kvl) || (a.causal && k0 + 31 > qw0)) {
+        const int lim = min(kvl, a.causal ? myq + 1 : kvl) - k0 - 4 * h;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + acc_row(r, h);
-          if (key >= kvl || (a.causal && key > myq)) s[r] = neg_inf();
-        }
+        for (int r = 0; r < 16; ++r)
+          if (acc_row(r, 0) >= lim) s[r] = neg_inf();
       }
-      float mx = neg_inf();
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      return max_halves(mx) * a.c;
+      return max16(s);
     };
     // Refresh the running max only when a score exceeds it by more than 2^TAU.
-    auto refresh = [&](float mt) {
-      if (wave_any(mt > m_run + TAU)) {
-        const float m_new = fmaxf(m_run, mt);
+    // The two lane halves hold different keys of the same query and share
+    // thr, so the test needs only the lane's own max; the max over both
+    // halves is formed inside the (rare) refresh.
+    auto refresh = [&](float lane_mx) {
+      if (wave_any(lane_mx > thr)) {
+        const float mx = max_halves(lane_mx);
+        const float m_new = fmaxf(m_run, mx * a.c);
         const float alpha = (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
@@ -151,6 +168,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[nb][r] *= alpha;
         m_run = m_new;
+        const bool live = m_new != neg_inf();
+        neg_mu = live ? -m_new : 0.f;
+        thr = live ? (m_new + TAU) * inv_c : neg_inf();
       }
     };
     // P~(t) from S(t) (in place), its row sum into l_run, and O^T += V^T P~^T.
@@ -158,14 +178,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // would halve the instruction count but does not co-execute with the
     // matrix core.)
     auto softmax_pv = [&](f32x16& s) {
-      const float mu = (m_run == neg_inf()) ? 0.f : m_run;
-      float ls = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -mu));
-        ls += s[r];
-      }
-      l_run += ls;
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, neg_mu));
+      float t8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t8[i] = s[2 * i] + s[2 * i + 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t8[i] += t8[i + 4];
+      l_run += (t8[0] + t8[2]) + (t8[1] + t8[3]);
       const PackedB pb = pack_bf16(s);
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb)
@@ -297,9 +317,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const bf16* Kg = reinterpret_cast<const bf16*>(a.k) + head;
     const float* lse_g = a.lse + (size_t)bh * N;
     const float* del_g = a.delta + (size_t)bh * N;
-    const auto rq = head_rsrc(reinterpret_cast<const bf16*>(a.q) + head, N, D);
-    const auto rg = head_rsrc(reinterpret_cast<const bf16*>(a.dO) + head, N, D);
-    const auto rv = head_rsrc(reinterpret_cast<const bf16*>(a.v) + head, N, D);
+    const bf16* Qh = reinterpret_cast<const bf16*>(a.q) + head;
+    const bf16* dOh = reinterpret_cast<const bf16*>(a.dO) + head;
+    const TileDma<D, C::BQ> dma;
 
     const int kw0 = kj * CELL + wave * 32;   // first key of this wave
     const int myk = kw0 + l32;               // the key this lane owns
@@ -321,8 +341,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     auto issue = [&](int it) {
       unsigned char* st = smem + C::VRES + (it & 1) * C::STAGE;
       const int q0 = walk.tile_start(it);
-      tile_load<D, C::BQ>(rq, q0, st);
-      tile_load<D, C::BQ>(rg, q0, st + C::TILE);
+      dma.load(Qh, N, q0, st);
+      dma.load(dOh, N, q0, st + C::TILE);
       if (tid < C::BQ) {
         const int q = q0 + tid;
         const float l = q < N ? lse_g[q] : neg_inf();
@@ -331,7 +351,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
     };
     if (walk.ntiles > 0) {
-      tile_load<D, CELL>(rv, kj * CELL, Vs);
+      TileDma<D, CELL>().load(reinterpret_cast<const bf16*>(a.v) + head, N, kj * CELL, Vs);
       issue(0);
     }
 
@@ -362,7 +382,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           mma(dp, as_bf16x8(row_chunk<D>(dOs, 32 * qs + l32, 2 * k + h)),
               as_bf16x8(row_chunk<D>(Vs, wave * 32 + l32, 2 * k + h)));
         }
-        // P = exp2(s c - lse log2 e), dS = P (dP - delta); register r <-> query 32 qs + acc_row(r, h)
+        // P = exp2(s c - lse log2 e), dS = P (dP - delta); register r <-> query
+        // q0 + 32 qs + acc_row(r, h).  On edge tiles an entry is masked iff the
+        // lane's key is at or past kv_len, or (causal) the key is past the
+        // query: acc_row(r, 0) < lim.
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int qq = 32 * qs + 8 * g + 4 * h;
@@ -371,11 +394,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -l4[e]));
-            if (edge && (myk >= kvl || (a.causal && myk > q0 + qq + e))) p = 0.f;
-            s[r] = p;
-            dp[r] = p * (dp[r] - d4[e]);
+            s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -l4[e]));
+            dp[r] = s[r] * (dp[r] - d4[e]);
           }
+        }
+        if (edge) {   // a masked entry has P = 0 and so dS = 0
+          const int lim = myk >= kvl ? CELL : (a.causal ? myk - q0 - 32 * qs - 4 * h : -1);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (acc_row(r, 0) < lim) s[r] = dp[r] = 0.f;
         }
         // dV^T += dO^T P and dK^T += Q^T dS, the transposed operands read from the row-major tiles
         const PackedB pb = pack_bf16(s), db = pack_bf16(dp);
@@ -495,8 +522,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const size_t head = (size_t)bh * N * D;
     const bf16* Qg = reinterpret_cast<const bf16*>(a.q) + head;
     const bf16* dOg = reinterpret_cast<const bf16*>(a.dO) + head;
-    const auto rk = head_rsrc(reinterpret_cast<const bf16*>(a.k) + head, N, D);
-    const auto rv = head_rsrc(reinterpret_cast<const bf16*>(a.v) + head, N, D);
+    const bf16* Kh = reinterpret_cast<const bf16*>(a.k) + head;
+    const bf16* Vh = reinterpret_cast<const bf16*>(a.v) + head;
+    const TileDma<D, 64> dma;
 
     const int qw0 = q_lo + wave * 32;
     const int myq = qw0 + l32;
@@ -522,8 +550,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     auto issue = [&](int it) {
       unsigned char* st = smem + (it & 1) * C::STAGE;
       const int kb0 = walk.tile_start(it);
-      tile_load<D, 64>(rk, kb0, st);
-      tile_load<D, 64>(rv, kb0, st + C::TILE);
+      dma.load(Kh, N, kb0, st);
+      dma.load(Vh, N, kb0, st + C::TILE);
     };
     if (walk.ntiles > 0) issue(0);
 
@@ -547,15 +575,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           mma(s, as_bf16x8(row_chunk<D>(Ks, 32 * sb + l32, 2 * k + h)), as_bf16x8(qf[k]));
           mma(dp, as_bf16x8(row_chunk<D>(Vs, 32 * sb + l32, 2 * k + h)), as_bf16x8(gf[k]));
         }
+        // register r holds key kb0 + 32 sb + acc_row(r, h): masked iff at or
+        // past kv_len or (causal) past the lane's query, i.e. acc_row(r, 0) >= lim
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -lse2));
-          if (edge) {
-            const int key = kb0 + 32 * sb + acc_row(r, h);
-            if (key >= kvl || (a.causal && key > myq)) p = 0.f;
-          }
-          dp[r] = p * (dp[r] - del);
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -lse2));
+        if (edge) {
+          const int lim = min(kvl, a.causal ? myq + 1 : kvl) - kb0 - 32 * sb - 4 * h;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (acc_row(r, 0) >= lim) s[r] = 0.f;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - del);
         // dQ^T += K^T dS^T, K^T read transposed from the row-major tile
         const PackedB db = pack_bf16(dp);
 #pragma unroll

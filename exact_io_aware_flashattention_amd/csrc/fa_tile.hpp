@@ -40,7 +40,7 @@ struct BTile {
   static constexpr int ROWB = D * 2;          // bytes per row
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 1024 / ROWB;   // rows one wave-wide load fills
-  __device__ static __forceinline__ int swz(int r) {
+  __host__ __device__ static constexpr int swz(int r) {
     return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
   }
   __device__ static __forceinline__ int off(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
@@ -49,13 +49,14 @@ struct BTile {
 // Index of the calling wave within the work-group, as a scalar.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// Buffer resource (V#) over rows [0, N) of one head ([N][D] bf16 at base):
-// base address, stride 0, num_records = N * D * 2 bytes, raw-buffer format bits.
-__device__ __forceinline__ u32x4 head_rsrc(const void* base, int N, int D) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
+// Buffer resource (V#) over rows [row0, N) of one head ([N][D] bf16 at head):
+// base address of row row0, stride 0, num_records = (N - row0) * D * 2 bytes,
+// raw-buffer format bits.  All fields are wave-uniform (scalar registers).
+__device__ __forceinline__ u32x4 rows_rsrc(const void* head, int N, int D, int row0) {
+  const uint64_t p = reinterpret_cast<uint64_t>(head) + (uint64_t)(uint32_t)row0 * (uint32_t)(D * 2);
   return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p),
                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu),
-               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(N * D * 2)), 0x00020000u};
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(max(N - row0, 0) * D * 2)), 0x00020000u};
 }
 
 // One wave-wide 16-byte-per-lane load into LDS at lds (+ 16 * lane).
@@ -67,26 +68,51 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, unsigned char* lds, int voff) 
                : "memory", "m0");
 }
 
-// Issue the loads of rows [row0, row0 + R) into the tile at lds (R * D * 2
-// bytes); the wave-wide loads are spread over the work-group's NW waves.
-// Completion: s_waitcnt vmcnt(0) in every wave, then a barrier.
-template <int D, int R, int NW = NT / 64>
-__device__ __forceinline__ void tile_load(u32x4 rsrc, int row0, unsigned char* lds) {
-  using TL = BTile<D>;
-  constexpr int NLOAD = R / TL::ROWS_PER_LOAD;
-  static_assert(NLOAD % NW == 0, "wave-wide loads must divide evenly over the waves");
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const int lr_in = lane / TL::CPR;          // row within one load
-  const int p = lane % TL::CPR;              // physical chunk
-#pragma unroll
-  for (int j = 0; j < NLOAD / NW; ++j) {
-    const int i = j * NW + wave;
-    const int lr = i * TL::ROWS_PER_LOAD + lr_in;
-    const int c = p ^ TL::swz(lr);
-    const int voff = ((row0 + lr) * D + c * 8) * 2;
-    dma16(rsrc, lds + i * 1024, voff);
-  }
+// Loads of an R-row tile spread over the NW waves of the work-group: wave w
+// issues the wave-wide loads i = j * NW + w (j < NJ), load i filling rows
+// [i * RPL, (i + 1) * RPL) (RPL rows per 1024 bytes).  The swizzle repeats
+// every NW * RPL rows (checked below), so the logical chunk a lane fetches is
+// the same for every j and the lane's byte offset inside the tile is
+// voff[0] + j * NW * 1024: the per-lane offsets are computed once per kernel,
+// and a tile load costs only scalar work (a buffer resource based at the
+// tile's first row) plus the load instructions.
+template <int D, int NW>
+__host__ __device__ constexpr bool swizzle_repeats(int nj) {
+  for (int w = 0; w < NW; ++w)
+    for (int r = 0; r < BTile<D>::ROWS_PER_LOAD; ++r)
+      for (int j = 0; j < nj; ++j)
+        if (BTile<D>::swz((j * NW + w) * BTile<D>::ROWS_PER_LOAD + r) != BTile<D>::swz(w * BTile<D>::ROWS_PER_LOAD + r))
+          return false;
+  return true;
 }
+
+template <int D, int R, int NW = NT / 64>
+struct TileDma {
+  using TL = BTile<D>;
+  static constexpr int NLOAD = R / TL::ROWS_PER_LOAD;
+  static constexpr int NJ = NLOAD / NW;
+  static_assert(NLOAD % NW == 0, "wave-wide loads must divide evenly over the waves");
+  static_assert(swizzle_repeats<D, NW>(NJ), "swizzle must repeat every NW loads");
+  int voff[NJ];
+
+  __device__ __forceinline__ TileDma() {
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int lr = wave * TL::ROWS_PER_LOAD + lane / TL::CPR;   // row of load j = 0
+    const int c = (lane % TL::CPR) ^ TL::swz(lr);               // logical chunk at position lane
+    const int off0 = (lr * D + c * 8) * 2;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) voff[j] = off0 + j * NW * 1024;
+  }
+  // Issue the loads of rows [row0, row0 + R) of head (N rows) into lds
+  // (R * D * 2 bytes); rows at or past N read as zeros.  Completion:
+  // s_waitcnt vmcnt(0) in every wave, then a barrier.
+  __device__ __forceinline__ void load(const void* head, int N, int row0, unsigned char* lds) const {
+    const u32x4 rsrc = rows_rsrc(head, N, D, row0);
+    const int wave = wave_id();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dma16(rsrc, lds + (j * NW + wave) * 1024, voff[j]);
+  }
+};
 
 __device__ __forceinline__ void wait_loads() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -20,7 +20,11 @@ struct Walk {
   int tsh;           // log2 of the tile width (32 or 64)
   const int* list;   // LDS list of visited cell offsets (block-sparse), or null
 
-  __device__ __forceinline__ int cell(int c) const { return base + (list ? list[c] : c); }
+  // (The list entry is wave-uniform; reading it as a scalar keeps all tile
+  // address arithmetic on the scalar unit.)
+  __device__ __forceinline__ int cell(int c) const {
+    return base + (list ? __builtin_amdgcn_readfirstlane(list[c]) : c);
+  }
   __device__ __forceinline__ int tile_start(int it) const {
     const int per = 7 - tsh;   // log2(tiles per cell)
     return cell(it >> per) * CELL + ((it & ((1 << per) - 1)) << tsh);
