@@ -12,8 +12,16 @@ Each stage is bracketed by HIP events recorded on the stream the library
 launches on, so the per-kernel averages come from the timed steps themselves.
 The roofline object describes the kernel with the largest average time.
 
-cpu_baseline times the fp64 CPU oracle (forward + backward) on one head of the
-same workload.
+cpu_baseline times the fp64 CPU oracle (forward + backward) on two heads of
+the same workload.
+
+--workload K times one of the other workloads (1 tiny fp32, 2 GPT-2 shaped,
+3 BERT-shaped with key padding, 5 block-sparse 64K) with the same step and
+prints the same kind of line (no CPU leg unless --cpu-baseline is given); the
+default line is the long-context workload.  Per kernel it reports achieved
+TFLOP/s against the bf16 matrix peak and achieved GB/s of compulsory HBM
+traffic against 8 TB/s, and names the bound of each kernel from its
+arithmetic intensity (compulsory bytes) against the ridge point.
 """
 from __future__ import annotations
 
@@ -30,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOP/s fwd+bwd (bf16, 1 GPU) and % of MFMA bf16 peak, N=1K–16K"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_TFLOPS = 157.3        # fp32 matrix peak
 
 
 def flops_fwd(B, H, N, d, causal, cell_frac=1.0):
@@ -37,11 +46,33 @@ def flops_fwd(B, H, N, d, causal, cell_frac=1.0):
     return f / 2 if causal else f
 
 
-def kernel_flops(name, B, H, N, d, causal):
-    """GEMM flops each kernel must execute per launch (visited score entries x 2d
-    per product): fwd 2 products (S, PV), dkdv 4 (S, dP, dV, dK), dq 3 (S, dP, dQ)."""
-    per_product = flops_fwd(B, H, N, d, causal) / 2
-    return {"fwd": 2, "dkdv": 4, "dq": 3, "pre": 0}[name] * per_product
+def workload_fwd_flops(w, inp):
+    """Forward attention flops of a workload: 4 B H N^2 d, halved for causal,
+    scaled by the fraction of nonzero mask cells and by mean(kv_len) / N."""
+    import numpy as np
+    f = flops_fwd(w.B, w.H, w.N, w.d, w.causal)
+    if inp.get("block_mask") is not None:
+        f *= float(np.asarray(inp["block_mask"]).sum()) / w.cells ** 2
+    if inp.get("kv_len") is not None:
+        f *= float(np.minimum(np.asarray(inp["kv_len"]), w.N).mean()) / w.N
+    return f
+
+
+PRODUCTS = {"fwd": 2, "dkdv": 4, "dq": 3, "pre": 0}
+
+
+def kernel_flops(name, f_fwd):
+    """GEMM flops a kernel executes per launch: score entries x 2d per product,
+    fwd 2 products (S, PV), dkdv 4 (S, dP, dV, dK), dq 3 (S, dP, dQ)."""
+    return PRODUCTS[name] * f_fwd / 2
+
+
+def kernel_bytes(name, B, H, N, d, esize):
+    """Compulsory HBM bytes per launch (each operand read once, each output
+    written once): the IO lower bound of the pages' complexity analysis."""
+    t, r = B * H * N * d * esize, B * H * N * 4
+    return {"fwd": 3 * t + t + r, "pre": 2 * t + r, "dkdv": 4 * t + 2 * r + 2 * t,
+            "dq": 4 * t + 2 * r + t}[name]
 
 
 def run_gpu_bench(w, steps, warmup, inp):
@@ -51,13 +82,18 @@ def run_gpu_bench(w, steps, warmup, inp):
     import exact_io_aware_flashattention_amd as fa
 
     dev = torch.device("cuda:0")
-    q, k, v, do = (torch.from_numpy(inp[n]).to(dev, torch.bfloat16) for n in ("q", "k", "v", "do"))
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v, do = (torch.from_numpy(inp[n]).to(dev, tdt) for n in ("q", "k", "v", "do"))
     B, H, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    kw = dict(scale=w.scale, causal=w.causal)
+    bm = None if inp.get("block_mask") is None else torch.from_numpy(np.ascontiguousarray(inp["block_mask"])).to(dev)
+    kl = None if inp.get("kv_len") is None else torch.from_numpy(inp["kv_len"].astype(np.int32)).to(dev)
+    ws_bytes = fa.fa_bwd_dkdv_workspace_bytes(N, d, fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32, bm is not None)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev) if ws_bytes else None
+    kw = dict(scale=w.scale, causal=w.causal, block_mask=bm, kv_len=kl)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -69,7 +105,7 @@ def run_gpu_bench(w, steps, warmup, inp):
         fa.fa_bwd_preprocess(o, do, delta, stream=stream)
         if ev:
             ev[2].record(stream)
-        fa.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, stream=stream, **kw)
+        fa.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, workspace=ws, stream=stream, **kw)
         if ev:
             ev[3].record(stream)
         fa.fa_bwd_dq(q, k, v, do, lse, delta, dq, stream=stream, **kw)
@@ -116,27 +152,29 @@ def copy_calibration():
 
 
 def cpu_baseline(w, inp, heads=2):
-    """fp64 oracle fwd + bwd on the first `heads` heads of the workload (all rows, all keys)."""
+    """fp64 oracle fwd + bwd on heads 0..heads-1 of batch entry 0 (all rows, all keys)."""
     import numpy as np
 
     from oracle import sparse
     cores = len(os.sched_getaffinity(0))
+    kv = None if inp.get("kv_len") is None else int(inp["kv_len"][0])
+    kw = dict(causal=w.causal, block_mask=inp.get("block_mask"), kv_len=kv)
     t0 = time.perf_counter()
     for h in range(heads):
         Q, K, V, dO = (inp[n][0, h].astype(np.float64) for n in ("q", "k", "v", "do"))
-        sparse.head_forward(Q, K, V, w.scale, causal=w.causal)
-        sparse.head_backward(Q, K, V, dO, w.scale, causal=w.causal)
+        sparse.head_forward(Q, K, V, w.scale, **kw)
+        sparse.head_backward(Q, K, V, dO, w.scale, **kw)
     dt = time.perf_counter() - t0
-    f = 3.5 * flops_fwd(1, heads, w.N, w.d, w.causal)
+    f = 3.5 * workload_fwd_flops(w, inp) * heads / (w.B * w.H)
     return {"value": round(f / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"heads 0-{heads - 1} of {w.B * w.H} of the same workload (N={w.N}, d={w.d}, causal), "
-                      f"fp64 forward+backward, {dt:.1f} s",
+            "sample": f"heads 0-{heads - 1} of batch entry 0 ({heads} of {w.B * w.H} heads) of the same workload "
+                      f"(N={w.N}, d={w.d}), fp64 forward+backward, {dt:.1f} s",
             "seconds": round(dt, 2)}
 
 
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "long_context_hbm_traffic.txt")
-KERNEL_SYMBOL = {"fwd": "fwd_bf16_kernel<128, false>", "dkdv": "dkdv_bf16_kernel<128, false>",
+KERNEL_SYMBOL = {"fwd": "fwd_bf16_kernel<128, false>", "dkdv": "dkdv_bf16_kernel<128, false, false>",
                  "dq": "dq_bf16_kernel<128, false>", "pre": "bwd_pre_kernel"}
 
 
@@ -203,12 +241,30 @@ def summarize_counters(fetch_csv, write_csv, command):
     print("\n".join(lines))
 
 
+def kernel_table(w, per, f_fwd, B, H, N, d):
+    """Per-kernel achieved TFLOP/s and compulsory-traffic GB/s, and the bound
+    implied by arithmetic intensity (flops per compulsory byte) against the
+    ridge point peak_flops / peak_bandwidth."""
+    esize = 2 if w.dtype == "bf16" else 4
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    out = {}
+    for n, ms in per.items():
+        fl, by = kernel_flops(n, f_fwd), kernel_bytes(n, B, H, N, d, esize)
+        out[n] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                  "hbm_gbs": round(by / (ms * 1e-3) / 1e9, 1), "alg_bytes": by,
+                  "bound": "mfma" if fl / by > ridge else "hbm"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, choices=(1, 2, 3, 4, 5),
+                    help="workload to time (default 4, the long-context line)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg (profiling runs)")
+    ap.add_argument("--cpu-baseline", action="store_true", help="run the CPU oracle leg for --workload other than 4")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, run one plain device copy of COPY_BYTES (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
@@ -223,34 +279,51 @@ def main():
         sys.exit(2)
 
     from workloads import WORKLOADS, digest, make_inputs
-    w = WORKLOADS[4]
+    w = WORKLOADS[args.workload]
     inp = make_inputs(w)
     if args.copy_calibration:
         copy_calibration()
     step_ms, per, wall, (B, H, N, d) = run_gpu_bench(w, args.steps, args.warmup, inp)
-    F = flops_fwd(B, H, N, d, w.causal)
+    F = workload_fwd_flops(w, inp)
     value = 3.5 * F / (step_ms * 1e-3) / 1e12
+    table = kernel_table(w, per, F, B, H, N, d)
 
     dom = max(("fwd", "dkdv", "dq"), key=lambda n: per[n])
-    ach = kernel_flops(dom, B, H, N, d, w.causal) / (per[dom] * 1e-3) / 1e12
-    fwd_ach = kernel_flops("fwd", B, H, N, d, w.causal) / (per["fwd"] * 1e-3) / 1e12
-    traffic = read_traffic()
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic.get(dom)}
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    if table[dom]["bound"] == "mfma":
+        ach = table[dom]["tflops"]
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(ach / peak, 4)}
+    else:
+        ach = table[dom]["hbm_gbs"]
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_HBM_GBS, 4)}
+    traffic = read_traffic() if args.workload == 4 else {}
+    roofline["traffic"] = traffic.get(dom)
+    desc = {1: "tiny exact: B=1 H=2 N=128 d=64 fp32, scale 1/8",
+            2: "GPT-2 shaped: B=8 H=12 N=1024 d=64 bf16 causal, scale 1/8",
+            3: "BERT-large shaped: B=32 H=16 N=512 d=64 bf16, key padding kv_len ~ U[128, 512], scale 1/8",
+            4: "long-context: B=1 H=16 N=16384 d=128 bf16 causal, scale 1/sqrt(128)",
+            5: "block-sparse: B=1 H=8 N=65536 d=64 bf16, 128x128 cell mask (band, 2 random cells per row, "
+               "first column), scale 1/8"}[args.workload]
+    config = {"workload": desc, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+              "input_sha256": digest(inp["q"], inp["k"], inp["v"])}
+    if inp.get("block_mask") is not None:
+        config["mask_cells"] = int(inp["block_mask"].sum())
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0, 0.5) Q/K/V/dO, inputs resident in HBM)",
-        "config": {"workload": "long-context: B=1 H=16 N=16384 d=128 bf16 causal, scale 1/sqrt(128)",
-                   "B": B, "H": H, "N": N, "d": d, "causal": True, "input_sha256": digest(inp["q"], inp["k"], inp["v"])},
-        "pct_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": f"synthetic (seeded N(0, {w.sigma ** 2:g}) Q/K/V/dO, inputs resident in HBM)",
+        "config": config,
+        "pct_mfma_peak": round(100 * value / peak, 2),
         "kernel_ms": {n: round(t, 4) for n, t in per.items()},
-        "fwd_tflops": round(fwd_ach, 2), "fwd_pct_mfma_peak": round(100 * fwd_ach / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": table["fwd"]["tflops"], "fwd_pct_mfma_peak": round(100 * table["fwd"]["tflops"] / peak, 2),
+        "kernels": table,
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if (args.workload == 4 and not args.no_cpu_baseline) or args.cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(out), flush=True)
 

@@ -1,0 +1,59 @@
+"""Host-side logic of bench.py (no GPU): the flop and byte conventions of the
+reported metric and the single-GPU guard."""
+import math
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from workloads import WORKLOADS  # noqa: E402
+
+
+def test_long_context_flops_follow_the_metric_definition():
+    w = WORKLOADS[4]
+    f = bench.workload_fwd_flops(w, {})
+    assert f == 4.0 * 1 * 16 * 16384 ** 2 * 128 / 2          # 4 B H N^2 d, halved for causal
+    assert math.isclose(f / 1e12, 1.0995, rel_tol=1e-4)
+    assert bench.kernel_flops("fwd", f) == f
+    assert bench.kernel_flops("dkdv", f) == 2 * f and bench.kernel_flops("dq", f) == 1.5 * f
+    # The metric counts the backward as 2.5 x forward (five products); the
+    # two-kernel backward executes seven (S and dP in both dK/dV and dQ), so
+    # the per-kernel figures are executed work, 3.5 x forward in total.
+    assert bench.kernel_flops("dkdv", f) + bench.kernel_flops("dq", f) == 3.5 * f
+
+
+def test_masked_workload_flops_scale_with_mask_and_padding():
+    w3, w5 = WORKLOADS[3], WORKLOADS[5]
+    kv = np.full(w3.B, 256, np.int32)
+    assert bench.workload_fwd_flops(w3, {"kv_len": kv}) == 4.0 * w3.B * w3.H * w3.N * 256 * w3.d
+    bm = np.zeros((w5.cells, w5.cells), np.uint8)
+    bm[:, 0] = 1
+    dense = 4.0 * w5.B * w5.H * w5.N ** 2 * w5.d
+    assert math.isclose(bench.workload_fwd_flops(w5, {"block_mask": bm}), dense / w5.cells)
+
+
+def test_compulsory_bytes():
+    B, H, N, d = 1, 16, 16384, 128
+    t, r = B * H * N * d * 2, B * H * N * 4
+    assert bench.kernel_bytes("fwd", B, H, N, d, 2) == 4 * t + r          # Q, K, V in; O, lse out
+    assert bench.kernel_bytes("dkdv", B, H, N, d, 2) == 6 * t + 2 * r     # Q, K, V, dO, lse, delta in; dK, dV out
+    assert bench.kernel_bytes("dq", B, H, N, d, 2) == 5 * t + 2 * r
+
+
+def test_bound_from_arithmetic_intensity():
+    w = WORKLOADS[4]
+    f = bench.workload_fwd_flops(w, {})
+    table = bench.kernel_table(w, {"fwd": 1.0, "pre": 0.02, "dkdv": 2.0, "dq": 1.5}, f, 1, 16, 16384, 128)
+    assert table["fwd"]["bound"] == "mfma" and table["pre"]["bound"] == "hbm"
+    assert math.isclose(table["fwd"]["tflops"], f / 1e-3 / 1e12, rel_tol=1e-3)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
