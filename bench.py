@@ -256,6 +256,32 @@ def kernel_table(w, per, f_fwd, B, H, N, d):
     return out
 
 
+def sweep(steps, warmup):
+    """The metric's N = 1K..16K range: N in {1K, 2K, 4K, 8K, 16K} with B = 16K / N,
+    H = 16, d in {64, 128}, causal off and on, bf16, scale 1/sqrt(d); Q/K/V/dO
+    i.i.d. N(0, 1) from one seeded draw (seed 6) per d, reshaped (B N is the
+    same for every N).  One JSON line per configuration."""
+    import numpy as np
+
+    from workloads import Workload, draw_qkvdo
+    for d in (64, 128):
+        flat = draw_qkvdo(1, 16, 16384, d, "bf16", 1.0, 6)
+        for N in (1024, 2048, 4096, 8192, 16384):
+            B = 16384 // N
+            inp = {n: a.reshape(B, 16, N, d) for n, a in zip(("q", "k", "v", "do"), flat)}
+            for causal in (False, True):
+                w = Workload(0, "sweep", B, 16, N, d, "bf16", causal, 1.0 / math.sqrt(d), 1.0)
+                step_ms, per, _, _ = run_gpu_bench(w, steps, warmup, inp)
+                F = workload_fwd_flops(w, inp)
+                t_bwd = per["pre"] + per["dkdv"] + per["dq"]
+                line = {"B": B, "H": 16, "N": N, "d": d, "causal": causal, "ms_per_step": round(step_ms, 4),
+                        "fwd_bwd_tflops": round(3.5 * F / (step_ms * 1e-3) / 1e12, 1),
+                        "fwd_tflops": round(F / (per["fwd"] * 1e-3) / 1e12, 1),
+                        "bwd_tflops": round(2.5 * F / (t_bwd * 1e-3) / 1e12, 1),
+                        "kernel_ms": {n: round(t, 4) for n, t in per.items()}}
+                print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +289,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=4, choices=(1, 2, 3, 4, 5),
                     help="workload to time (default 4, the long-context line)")
+    ap.add_argument("--sweep", action="store_true", help="time the N = 1K..16K sweep (one JSON line per shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg (profiling runs)")
     ap.add_argument("--cpu-baseline", action="store_true", help="run the CPU oracle leg for --workload other than 4")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -277,6 +304,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the attention hot path here is "
               f"single-GPU and has no multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        sweep(args.steps, args.warmup)
+        return
 
     from workloads import WORKLOADS, digest, make_inputs
     w = WORKLOADS[args.workload]

@@ -68,9 +68,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   const int N = a.N;
   const int T_cells = (N + CELL - 1) / CELL;
-  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int bh = L / T_cells, tq = L - bh * T_cells;
-  const int qi = a.causal ? T_cells - 1 - tq : tq;   // heaviest causal rows first
+  const WorkUnit u = work_unit(blockIdx.x, gridDim.x, a.B * a.H, T_cells, a.causal);
+  const int bh = u.bh;
+  const int qi = a.causal ? T_cells - 1 - u.t : u.t;   // heaviest causal rows first
   const int b = bh / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
@@ -290,9 +290,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     c0 = (r - e[1]) * ch;
   } else {
     const int off = SPLIT ? SPLIT_MAX_ITEMS : 0;
-    const int L = xcd_logical_id(blockIdx.x - off, gridDim.x - off);
-    bh = L / T_cells;
-    kj = L - bh * T_cells;
+    const WorkUnit u = work_unit(blockIdx.x - off, gridDim.x - off, a.B * a.H, T_cells, a.causal);
+    bh = u.bh;
+    kj = u.t;   // causal: low kj sees the most queries
   }
   const int b = bh / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -502,9 +502,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   const int N = a.N;
   const int T_cells = (N + CELL - 1) / CELL;
-  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int bh = L / T_cells, tq = L - bh * T_cells;
-  const int qi = a.causal ? T_cells - 1 - tq : tq;
+  const WorkUnit u = work_unit(blockIdx.x, gridDim.x, a.B * a.H, T_cells, a.causal);
+  const int bh = u.bh;
+  const int qi = a.causal ? T_cells - 1 - u.t : u.t;
   const int b = bh / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;

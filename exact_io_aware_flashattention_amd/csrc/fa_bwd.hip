@@ -173,8 +173,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DkdvCfg<T, D
 
   const int N = a.N;
   const int T_cells = (N + CELL - 1) / CELL;
-  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int bh = L / T_cells, kj = L - bh * T_cells;   // causal: low kj sees the most queries
+  const WorkUnit u = work_unit(blockIdx.x, gridDim.x, a.B * a.H, T_cells, a.causal);
+  const int bh = u.bh, kj = u.t;   // causal: low kj sees the most queries
   const int b = bh / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -348,9 +348,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occ<T>::W, O
 
   const int N = a.N;
   const int T_cells = (N + CELL - 1) / CELL;
-  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int bh = L / T_cells, tq = L - bh * T_cells;
-  const int qi = a.causal ? T_cells - 1 - tq : tq;
+  const WorkUnit u = work_unit(blockIdx.x, gridDim.x, a.B * a.H, T_cells, a.causal);
+  const int bh = u.bh;
+  const int qi = a.causal ? T_cells - 1 - u.t : u.t;
   const int b = bh / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;

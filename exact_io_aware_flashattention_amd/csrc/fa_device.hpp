@@ -185,6 +185,24 @@ __device__ __forceinline__ int xcd_logical_id(int w, int n) {
   return (x < rem) ? x * (per + 1) + k : rem * (per + 1) + (x - rem) * per + k;
 }
 
+// (head, step) of work-group w of n = BH * T.  The step t indexes the cells
+// along the walked direction; for a causal walk step 0 is the heaviest (the
+// caller maps it to the last query cell or the first key cell).
+//   causal:     t = w / BH, head = w % BH.  All heads' heaviest cells are
+//               dispatched first, so no heavy cell is left to start at the end;
+//               and since work-group w goes to XCD w % 8, an XCD keeps serving
+//               the heads head = XCD (mod 8) when 8 divides BH.
+//   non-causal: equal work per cell; XCD-contiguous ranges of one head
+//               (xcd_logical_id) keep each head's K/V stream in one L2.
+struct WorkUnit {
+  int bh, t;
+};
+__device__ __forceinline__ WorkUnit work_unit(int w, int n, int BH, int T, bool causal) {
+  if (causal) return WorkUnit{w % BH, w / BH};
+  const int L = xcd_logical_id(w, n);
+  return WorkUnit{L / T, L % T};
+}
+
 // Build, in LDS, the ascending list of indices c in [0, count) with
 // pred(c) true.  All threads of the work-group must call it.  Returns the
 // list length (same value in every thread).

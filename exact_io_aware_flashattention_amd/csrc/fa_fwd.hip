@@ -52,9 +52,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occ<T>::W, O
 
   const int N = a.N;
   const int T_cells = (N + CELL - 1) / CELL;
-  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int bh = L / T_cells, tq = L - bh * T_cells;
-  const int qi = a.causal ? T_cells - 1 - tq : tq;   // heaviest causal rows first
+  const WorkUnit u = work_unit(blockIdx.x, gridDim.x, a.B * a.H, T_cells, a.causal);
+  const int bh = u.bh;
+  const int qi = a.causal ? T_cells - 1 - u.t : u.t;   // heaviest causal rows first
   const int b = bh / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;

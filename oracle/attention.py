@@ -31,16 +31,18 @@ import numpy as np
 CELL = 128
 
 
-def allowed(rows, nk, causal=False, block_mask=None, kv_len=None, cell=CELL):
+def allowed(rows, nk, causal=False, block_mask=None, kv_len=None, cell=CELL, keys=None):
     """Boolean [len(rows), nk]; True where key j may be attended by query i.
 
     causal: j <= i (queries and keys share positions, top-left aligned).
     kv_len: j < kv_len (key padding).
     block_mask: block_mask[i // cell, j // cell] == 1 (block-sparse cells,
     FlashAttention reading guide "Ekstensi: Block-Sparse FlashAttention").
-    The three conditions are combined with AND."""
+    The three conditions are combined with AND.  With ``keys`` given, the
+    columns are those key positions instead of 0 .. nk-1."""
     i = np.asarray(rows, dtype=np.int64)[:, None]
-    j = np.arange(nk, dtype=np.int64)[None, :]
+    j = (np.arange(nk, dtype=np.int64) if keys is None else np.asarray(keys, dtype=np.int64))[None, :]
+    nk = j.shape[1]
     ok = np.ones((i.shape[0], nk), dtype=bool)
     if causal:
         ok &= j <= i

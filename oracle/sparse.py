@@ -25,21 +25,19 @@ def cell_keys(i_cell, N, causal, block_mask, kv_len, cell=CELL):
     """Key positions of the surviving cells of query cell i_cell, ascending."""
     T = -(-N // cell)
     L = N if kv_len is None else int(kv_len)
-    keys = []
-    for j in range(T):
-        if block_mask is not None and not block_mask[i_cell][j]:
-            continue
-        if causal and j > i_cell:
-            continue
-        if cell * j >= L:
-            continue
-        keys.append(np.arange(cell * j, min(N, cell * (j + 1))))
+    j = np.arange(T)
+    keep = (j * cell < L)
+    if block_mask is not None:
+        keep &= np.asarray(block_mask[i_cell]).astype(bool)
+    if causal:
+        keep &= j <= i_cell
+    keys = [np.arange(cell * c, min(N, cell * (c + 1))) for c in np.flatnonzero(keep)]
     return np.concatenate(keys) if keys else np.zeros(0, np.int64)
 
 
 def _row_probs(Q, K, rows, keys, scale, causal, block_mask, kv_len):
     S = scale * (Q[rows] @ K[keys].T)
-    ok = allowed(rows, K.shape[0], causal, block_mask, kv_len)[:, keys]
+    ok = allowed(rows, K.shape[0], causal, block_mask, kv_len, keys=keys)
     return _probs(np.where(ok, S, -np.inf))
 
 

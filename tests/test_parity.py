@@ -171,6 +171,34 @@ def test_split_key_columns(case):
         assert np.all(out["dk"][1, :, kv[1]:] == 0) and np.all(out["dv"][1, :, kv[1]:] == 0)
 
 
+def test_maximum_mask_size():
+    """The largest block mask the library accepts: T = 2048 cells per side
+    (N = 262144), causal band mask with a global first column (split in
+    dK/dV).  Sampled rows of O, lse, dQ and sampled key columns of dK, dV
+    (including the global column) against the gathered oracle."""
+    N, d = 2048 * 128, 64
+    bm = band_random_mask(2048, 2200, n_random=1)
+    q, k, v, do = draw_qkvdo(1, 1, N, d, "bf16", 1.0, 2201)
+    inp = dict(q=q, k=k, v=v, do=do, kv_len=None, block_mask=bm, B=1, H=1, N=N, d=d, dtype="bf16",
+               causal=True, scale=0.125)
+    say(f"maximum mask size: N={N} T=2048 cells={int(bm.sum())}")
+    out = run_gpu(inp)
+    for n in ("o", "dq", "dk", "dv"):
+        assert np.all(np.isfinite(out[n])), n
+    rng = np.random.Generator(np.random.PCG64(2202))
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, N // 2, N - 129, N - 1], rng.integers(0, N, 25)]))
+    cols = np.unique(np.concatenate([[0, 1, 127, 128, N - 1], rng.integers(0, N, 11)]))
+    Q, K, V, dO = q[0, 0], k[0, 0], v[0, 0], do[0, 0]
+    kw = dict(causal=True, block_mask=bm, kv_len=None)
+    O, lse = sparse.head_forward_rows(Q, K, V, 0.125, rows, **kw)
+    compare_forward(out["o"][0, 0][rows], out["lse"][0, 0][rows], O, lse, "bf16", "max-size rows")
+    compare_grad(out["dq"][0, 0][rows], sparse.head_backward_rows(Q, K, V, dO, 0.125, rows, **kw), "bf16",
+                 "max-size dq rows")
+    _, dK, dV = sparse.head_backward(Q, K, V, dO, 0.125, key_cols=cols, **kw)
+    compare_grad(out["dk"][0, 0][cols], dK, "bf16", "max-size dk cols")
+    compare_grad(out["dv"][0, 0][cols], dV, "bf16", "max-size dv cols")
+
+
 def test_empty_problem_is_a_no_op():
     import torch
 
@@ -210,6 +238,22 @@ def test_workload_full_size_sampled_heads(key):
     for n in ("o", "dq", "dk", "dv"):
         assert np.all(np.isfinite(out[n])), n
     _check_heads_dense(inp, out, _sample_heads(inp["B"], inp["H"], 6, key), f"w{key}")
+
+
+@pytest.mark.parametrize("shape", [(2048, 128, False), (4096, 64, True)], ids=["N2048d128", "N4096d64c"])
+def test_sweep_shapes_sampled_heads(shape):
+    """Shapes of the N = 1K..16K sweep timed by bench.py --sweep (B = 16K / N,
+    H = 16, the same seeded draw reshaped), on sampled heads against the dense
+    oracle."""
+    N, d, causal = shape
+    B = 16384 // N
+    flat = draw_qkvdo(1, 16, 16384, d, "bf16", 1.0, 6)
+    q, k, v, do = (a.reshape(B, 16, N, d) for a in flat)
+    inp = dict(q=q, k=k, v=v, do=do, kv_len=None, block_mask=None, B=B, H=16, N=N, d=d, dtype="bf16",
+               causal=causal, scale=1.0 / np.sqrt(d))
+    say(f"sweep shape B={B} H=16 N={N} d={d} causal={causal}")
+    out = run_gpu(inp)
+    _check_heads_dense(inp, out, _sample_heads(B, 16, 3, N + d), f"sweep N{N}d{d}")
 
 
 @pytest.mark.parametrize("key", [4, 5])

@@ -43,6 +43,8 @@ CASES = [
     # key columns 0 and 20 visited by every query cell: the dK/dV walk splits them
     (2, 2, 5083, 64, False, "split", [5083, 1000]),
     (1, 2, 5083, 128, True, "split", None),
+    # the largest mask accepted: 2048 x 2048 cells
+    (1, 1, 2048 * 128, 64, True, "band", None),
 ]
 
 
