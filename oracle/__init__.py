@@ -20,5 +20,7 @@ Modules:
   online     the incremental softmax statistics and the tiled forward as the
              pages state them -- used by the pin tests to show exactness
   visits     the expected set of visited (query cell, key cell) pairs
+  dropout    the definition with dropout on P (Philox4x32-10 random bytes),
+             forward and backward
 """
-from . import attention, online, sparse, visits  # noqa: F401
+from . import attention, dropout, online, sparse, visits  # noqa: F401
