@@ -22,7 +22,7 @@ WALK_FWD, WALK_DKDV, WALK_DQ = 0, 1, 2
 CELL = 128
 
 EXPORTS = ("fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd_dkdv_workspace_bytes", "fa_bwd", "fa_bwd_preprocess",
-           "fa_bwd_dkdv", "fa_bwd_dq", "fa_debug_visits", "fa_status_str")
+           "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_dropout", "fa_bwd_dropout", "fa_debug_visits", "fa_status_str")
 
 
 class FAError(RuntimeError):
@@ -47,7 +47,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     except ImportError:
         pass
     lib = ctypes.CDLL(path)
-    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    P, I, F, S, U64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_uint64
     sig = {
         "fa_fwd": [P, P, P, P, P, I, I, I, I, F, I, P, P, I, P],
         "fa_bwd_workspace_bytes": [I, I, I, I, I, I],
@@ -56,6 +56,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fa_bwd_preprocess": [P, P, P, I, I, I, I, I, P],
         "fa_bwd_dkdv": [P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, P, S, P],
         "fa_bwd_dq": [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, P],
+        "fa_fwd_dropout": [P, P, P, P, P, I, I, I, I, F, I, P, P, I, F, U64, P],
+        "fa_bwd_dropout": [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, F, U64, P, S, P],
         "fa_debug_visits": [I, I, I, I, I, I, P, P, I, P, P, S, P],
         "fa_status_str": [I],
     }
@@ -129,9 +131,11 @@ def _scale(scale, d):
 # ---------------------------------------------------------------- entry points
 
 def fa_fwd(q, k, v, o=None, lse=None, *, scale=None, causal=False, block_mask=None, kv_len=None,
-           stream=None):
+           dropout_p=0.0, seed=0, stream=None):
     """O, lse = attention forward.  q, k, v: [B,H,N,d] bf16 or float32 on the GPU;
-    block_mask: uint8 [T,T] (T = ceil(N/128)) or None; kv_len: int32 [B] or None."""
+    block_mask: uint8 [T,T] (T = ceil(N/128)) or None; kv_len: int32 [B] or None;
+    dropout_p > 0 applies dropout on P (bf16 only; rate rounded to a multiple
+    of 1/256) with the Philox stream of `seed`."""
     import torch
     B, H, N, d = _shape(q)
     if o is None:
@@ -140,8 +144,12 @@ def fa_fwd(q, k, v, o=None, lse=None, *, scale=None, causal=False, block_mask=No
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check_like(q, q, k, v, o, lse, block_mask, kv_len)
     mb, kl = _mask_args(block_mask, kv_len)
-    _call("fa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _scale(scale, d),
-          int(bool(causal)), mb, kl, _dtype_code(q), _stream(stream))
+    if dropout_p:
+        _call("fa_fwd_dropout", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _scale(scale, d),
+              int(bool(causal)), mb, kl, _dtype_code(q), float(dropout_p), int(seed), _stream(stream))
+    else:
+        _call("fa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _scale(scale, d),
+              int(bool(causal)), mb, kl, _dtype_code(q), _stream(stream))
     return o, lse
 
 
@@ -163,8 +171,9 @@ def _workspace(workspace, need, device):
 
 
 def fa_bwd(q, k, v, o, dO, lse, dq=None, dk=None, dv=None, *, scale=None, causal=False, block_mask=None,
-           kv_len=None, workspace=None, stream=None):
-    """dQ, dK, dV for the loss gradient dO, from the forward's O and lse."""
+           kv_len=None, dropout_p=0.0, seed=0, workspace=None, stream=None):
+    """dQ, dK, dV for the loss gradient dO, from the forward's O and lse (with
+    the same dropout_p and seed as the forward)."""
     import torch
     B, H, N, d = _shape(q)
     dq = torch.empty_like(q) if dq is None else dq
@@ -174,9 +183,14 @@ def fa_bwd(q, k, v, o, dO, lse, dq=None, dk=None, dv=None, *, scale=None, causal
     workspace, ws_bytes = _workspace(workspace, max(need, 256), q.device)
     _check_like(q, q, k, v, o, dO, lse, dq, dk, dv, workspace, block_mask, kv_len)
     mb, kl = _mask_args(block_mask, kv_len)
-    _call("fa_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-          B, H, N, d, _scale(scale, d), int(bool(causal)), mb, kl, _dtype_code(q), _ptr(workspace),
-          ws_bytes, _stream(stream))
+    if dropout_p:
+        _call("fa_bwd_dropout", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
+              _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)), mb, kl, _dtype_code(q),
+              float(dropout_p), int(seed), _ptr(workspace), ws_bytes, _stream(stream))
+    else:
+        _call("fa_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+              B, H, N, d, _scale(scale, d), int(bool(causal)), mb, kl, _dtype_code(q), _ptr(workspace),
+              ws_bytes, _stream(stream))
     return dq, dk, dv
 
 

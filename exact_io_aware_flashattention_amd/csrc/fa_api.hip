@@ -77,6 +77,31 @@ fa::AttnArgs make_args(const Shape& s, float scale, int causal, const uint8_t* b
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// Dropout request: p in [0, 1) becomes the byte threshold t = round(256 p)
+// (keep iff the random byte >= t, so the effective rate is t / 256); t must
+// be at most 255.  t = 0 is no dropout.  Only the bf16 kernels implement it.
+struct Drop {
+  uint32_t t = 0;
+  uint64_t seed = 0;
+};
+
+int make_drop(float p, uint64_t seed, int dtype, Drop* out) {
+  if (!isfinite(p) || p < 0.f || p >= 1.f) return FA_ERR_ARG;
+  const long t = lrintf(p * 256.f);
+  if (t > 255) return FA_ERR_ARG;
+  if (t > 0 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  out->t = (uint32_t)t;
+  out->seed = seed;
+  return FA_OK;
+}
+
+void set_drop(fa::AttnArgs& a, const Drop& d) {
+  a.drop_t = d.t;
+  a.drop_k0 = (uint32_t)(d.seed & 0xffffffffu);
+  a.drop_k1 = (uint32_t)(d.seed >> 32);
+  a.drop_inv = 256.f / (256.f - (float)d.t);
+}
+
 size_t delta_bytes(int B, int H, int N) {
   const size_t bytes = (size_t)B * H * N * sizeof(float);
   return (bytes + 255) & ~(size_t)255;
@@ -99,6 +124,120 @@ int split_workspace(fa::AttnArgs& a, const Shape& s, void* ws, size_t ws_bytes) 
     if (_st != FA_OK) return _st; \
   } while (0)
 
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+             float scale, int causal, const uint8_t* block_mask, const int32_t* kv_len, int dtype, const Drop& drop,
+             void* stream) {
+  const Shape s{B, H, N, d, dtype};
+  bool empty = false;
+  FA_TRY(check_shape(s, block_mask, &empty));
+  if (empty) return FA_OK;
+  FA_TRY(check_tensors({q, k, v, o}));
+  FA_TRY(check_rowstats({lse}));
+  FA_TRY(check_masks(block_mask, kv_len));
+  FA_TRY(check_scale(scale));
+  fa::AttnArgs a = make_args(s, scale, causal, block_mask, kv_len);
+  set_drop(a, drop);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out0 = o;
+  a.lse = lse;
+  return hip_status(fa::launch_fwd(a, dtype, d, false, static_cast<hipStream_t>(stream)));
+}
+
+int dkdv_impl(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+              void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, const uint8_t* block_mask,
+              const int32_t* kv_len, int dtype, const Drop& drop, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  const Shape s{B, H, N, d, dtype};
+  bool empty = false;
+  FA_TRY(check_shape(s, block_mask, &empty));
+  if (empty) return FA_OK;
+  FA_TRY(check_tensors({q, k, v, dO, dk, dv}));
+  FA_TRY(check_rowstats({lse, delta}));
+  FA_TRY(check_masks(block_mask, kv_len));
+  FA_TRY(check_scale(scale));
+  fa::AttnArgs a = make_args(s, scale, causal, block_mask, kv_len);
+  set_drop(a, drop);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dO = dO;
+  a.lse = const_cast<float*>(lse);
+  a.delta = const_cast<float*>(delta);
+  a.out0 = dk;
+  a.out1 = dv;
+  FA_TRY(split_workspace(a, s, workspace, workspace_bytes));
+  return hip_status(fa::launch_bwd_dkdv(a, dtype, d, false, static_cast<hipStream_t>(stream)));
+}
+
+int dq_impl(const void* q, const void* k, const void* v, const void* dO, const float* lse, const float* delta,
+            void* dq, int B, int H, int N, int d, float scale, int causal, const uint8_t* block_mask,
+            const int32_t* kv_len, int dtype, const Drop& drop, void* stream) {
+  const Shape s{B, H, N, d, dtype};
+  bool empty = false;
+  FA_TRY(check_shape(s, block_mask, &empty));
+  if (empty) return FA_OK;
+  FA_TRY(check_tensors({q, k, v, dO, dq}));
+  FA_TRY(check_rowstats({lse, delta}));
+  FA_TRY(check_masks(block_mask, kv_len));
+  FA_TRY(check_scale(scale));
+  fa::AttnArgs a = make_args(s, scale, causal, block_mask, kv_len);
+  set_drop(a, drop);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dO = dO;
+  a.lse = const_cast<float*>(lse);
+  a.delta = const_cast<float*>(delta);
+  a.out0 = dq;
+  return hip_status(fa::launch_bwd_dq(a, dtype, d, false, static_cast<hipStream_t>(stream)));
+}
+
+
+int pre_impl(const void* o, const void* dO, float* delta, int B, int H, int N, int d, int dtype,
+                      void* stream) {
+  const Shape s{B, H, N, d, dtype};
+  bool empty = false;
+  FA_TRY(check_shape(s, nullptr, &empty));
+  if (empty) return FA_OK;
+  FA_TRY(check_tensors({o, dO}));
+  FA_TRY(check_rowstats({delta}));
+  fa::AttnArgs a = make_args(s, 1.f, 0, nullptr, nullptr);
+  a.o = o;
+  a.dO = dO;
+  a.delta = delta;
+  return hip_status(fa::launch_bwd_pre(a, dtype, d, static_cast<hipStream_t>(stream)));
+}
+
+size_t split_bytes(int N, int d, int dtype, int has_block_mask) {
+  if (N <= 0 || (d != 64 && d != 128) || dtype != FA_BF16 || !has_block_mask) return 0;
+  return fa::split_ws_bytes(N, d);
+}
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+             void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+             const uint8_t* block_mask, const int32_t* kv_len, int dtype, const Drop& drop, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  const Shape s{B, H, N, d, dtype};
+  bool empty = false;
+  FA_TRY(check_shape(s, block_mask, &empty));
+  if (empty) return FA_OK;
+  FA_TRY(check_tensors({q, k, v, o, dO, dq, dk, dv}));
+  FA_TRY(check_rowstats({lse}));
+  FA_TRY(check_masks(block_mask, kv_len));
+  FA_TRY(check_scale(scale));
+  if (!workspace) return FA_ERR_NULL;
+  if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+  const size_t db = delta_bytes(B, H, N);
+  if (workspace_bytes < db + split_bytes(N, d, dtype, block_mask != nullptr)) return FA_ERR_WORKSPACE;
+  float* delta = static_cast<float*>(workspace);
+  FA_TRY(pre_impl(o, dO, delta, B, H, N, d, dtype, stream));
+  FA_TRY(dkdv_impl(q, k, v, dO, lse, delta, dk, dv, B, H, N, d, scale, causal, block_mask, kv_len, dtype, drop,
+                   static_cast<unsigned char*>(workspace) + db, workspace_bytes - db, stream));
+  return dq_impl(q, k, v, dO, lse, delta, dq, B, H, N, d, scale, causal, block_mask, kv_len, dtype, drop, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -118,119 +257,63 @@ const char* fa_status_str(int status) {
 }
 
 size_t fa_bwd_dkdv_workspace_bytes(int N, int d, int dtype, int has_block_mask) {
-  if (N <= 0 || (d != 64 && d != 128) || dtype != FA_BF16 || !has_block_mask) return 0;
-  return fa::split_ws_bytes(N, d);
+  return split_bytes(N, d, dtype, has_block_mask);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int has_block_mask) {
   if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return delta_bytes(B, H, N) + fa_bwd_dkdv_workspace_bytes(N, d, dtype, has_block_mask);
+  return delta_bytes(B, H, N) + split_bytes(N, d, dtype, has_block_mask);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
            float scale, int causal, const uint8_t* block_mask, const int32_t* kv_len, int dtype,
            void* stream) {
-  const Shape s{B, H, N, d, dtype};
-  bool empty = false;
-  FA_TRY(check_shape(s, block_mask, &empty));
-  if (empty) return FA_OK;
-  FA_TRY(check_tensors({q, k, v, o}));
-  FA_TRY(check_rowstats({lse}));
-  FA_TRY(check_masks(block_mask, kv_len));
-  FA_TRY(check_scale(scale));
-  fa::AttnArgs a = make_args(s, scale, causal, block_mask, kv_len);
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.out0 = o;
-  a.lse = lse;
-  return hip_status(fa::launch_fwd(a, dtype, d, false, static_cast<hipStream_t>(stream)));
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, kv_len, dtype, Drop{}, stream);
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, const uint8_t* block_mask, const int32_t* kv_len, int dtype,
+                   float dropout_p, uint64_t seed, void* stream) {
+  Drop drop;
+  FA_TRY(make_drop(dropout_p, seed, dtype, &drop));
+  return fwd_impl(q, k, v, o, lse, B, H, N, d, scale, causal, block_mask, kv_len, dtype, drop, stream);
 }
 
 int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H, int N, int d, int dtype,
                       void* stream) {
-  const Shape s{B, H, N, d, dtype};
-  bool empty = false;
-  FA_TRY(check_shape(s, nullptr, &empty));
-  if (empty) return FA_OK;
-  FA_TRY(check_tensors({o, dO}));
-  FA_TRY(check_rowstats({delta}));
-  fa::AttnArgs a = make_args(s, 1.f, 0, nullptr, nullptr);
-  a.o = o;
-  a.dO = dO;
-  a.delta = delta;
-  return hip_status(fa::launch_bwd_pre(a, dtype, d, static_cast<hipStream_t>(stream)));
+  return pre_impl(o, dO, delta, B, H, N, d, dtype, stream);
 }
 
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                 const float* delta, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
                 const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  const Shape s{B, H, N, d, dtype};
-  bool empty = false;
-  FA_TRY(check_shape(s, block_mask, &empty));
-  if (empty) return FA_OK;
-  FA_TRY(check_tensors({q, k, v, dO, dk, dv}));
-  FA_TRY(check_rowstats({lse, delta}));
-  FA_TRY(check_masks(block_mask, kv_len));
-  FA_TRY(check_scale(scale));
-  fa::AttnArgs a = make_args(s, scale, causal, block_mask, kv_len);
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.dO = dO;
-  a.lse = const_cast<float*>(lse);
-  a.delta = const_cast<float*>(delta);
-  a.out0 = dk;
-  a.out1 = dv;
-  FA_TRY(split_workspace(a, s, workspace, workspace_bytes));
-  return hip_status(fa::launch_bwd_dkdv(a, dtype, d, false, static_cast<hipStream_t>(stream)));
+  return dkdv_impl(q, k, v, dO, lse, delta, dk, dv, B, H, N, d, scale, causal, block_mask, kv_len, dtype, Drop{},
+                   workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
               const float* delta, void* dq, int B, int H, int N, int d, float scale, int causal,
               const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* stream) {
-  const Shape s{B, H, N, d, dtype};
-  bool empty = false;
-  FA_TRY(check_shape(s, block_mask, &empty));
-  if (empty) return FA_OK;
-  FA_TRY(check_tensors({q, k, v, dO, dq}));
-  FA_TRY(check_rowstats({lse, delta}));
-  FA_TRY(check_masks(block_mask, kv_len));
-  FA_TRY(check_scale(scale));
-  fa::AttnArgs a = make_args(s, scale, causal, block_mask, kv_len);
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.dO = dO;
-  a.lse = const_cast<float*>(lse);
-  a.delta = const_cast<float*>(delta);
-  a.out0 = dq;
-  return hip_status(fa::launch_bwd_dq(a, dtype, d, false, static_cast<hipStream_t>(stream)));
+  return dq_impl(q, k, v, dO, lse, delta, dq, B, H, N, d, scale, causal, block_mask, kv_len, dtype, Drop{}, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
            void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
            const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* workspace,
            size_t workspace_bytes, void* stream) {
-  const Shape s{B, H, N, d, dtype};
-  bool empty = false;
-  FA_TRY(check_shape(s, block_mask, &empty));
-  if (empty) return FA_OK;
-  FA_TRY(check_tensors({q, k, v, o, dO, dq, dk, dv}));
-  FA_TRY(check_rowstats({lse}));
-  FA_TRY(check_masks(block_mask, kv_len));
-  FA_TRY(check_scale(scale));
-  if (!workspace) return FA_ERR_NULL;
-  if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
-  if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d, dtype, block_mask != nullptr))
-    return FA_ERR_WORKSPACE;
-  float* delta = static_cast<float*>(workspace);
-  const size_t db = delta_bytes(B, H, N);
-  FA_TRY(fa_bwd_preprocess(o, dO, delta, B, H, N, d, dtype, stream));
-  FA_TRY(fa_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, B, H, N, d, scale, causal, block_mask, kv_len, dtype,
-                     static_cast<unsigned char*>(workspace) + db, workspace_bytes - db, stream));
-  return fa_bwd_dq(q, k, v, dO, lse, delta, dq, B, H, N, d, scale, causal, block_mask, kv_len, dtype, stream);
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, block_mask, kv_len, dtype, Drop{},
+                  workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* block_mask, const int32_t* kv_len, int dtype, float dropout_p, uint64_t seed,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  Drop drop;
+  FA_TRY(make_drop(dropout_p, seed, dtype, &drop));
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, block_mask, kv_len, dtype, drop,
+                  workspace, workspace_bytes, stream);
 }
 
 int fa_debug_visits(int which, int B, int H, int N, int d, int causal, const uint8_t* block_mask,

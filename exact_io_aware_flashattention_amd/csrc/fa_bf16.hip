@@ -16,6 +16,7 @@
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 #include "fa_tile.hpp"
+#include "fa_dropout.hpp"
 #include "fa_walk.hpp"
 
 #include <type_traits>
@@ -25,6 +26,10 @@ namespace fa {
 // Scores of one 32 x 32 block in accumulator layout: register r of lane l
 // belongs to the key/query pair (8*(r/4) + 4*h + r%4, l % 32).
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Kernel instances: the attention arithmetic, the tile walk alone (visit
+// counters), or the arithmetic with dropout on P.
+constexpr int K_PLAIN = 0, K_WALK = 1, K_DROP = 2;
 
 // Scheduling hint for a branch-free region holding 16 MFMAs and the VALU work
 // of one 32-key sub-block: alternate one MFMA with up to six VALU
@@ -70,9 +75,11 @@ struct FwdB {
 // K and V tiles have separate two-deep LDS rings.  Per 64-key tile j there is
 // one barrier and one DMA issue (K of tile j+2, V of tile j+1), so every tile
 // is requested two sub-block steps before it is read.
-template <int D, bool WALK_ONLY>
+template <int D, int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(AttnArgs a) {
   using C = FwdB<D>;
+  constexpr bool WALK_ONLY = MODE == K_WALK, DROP = MODE == K_DROP;
+  __shared__ u32x4 drop_xch[DROP ? NT : 1];
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[WALK_ONLY ? 16 : 2 * C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf[WALK_ONLY ? 16 : 2 * C::TILE];
   __shared__ int cell_list[MAX_T];
@@ -188,8 +195,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // P~(t) from S(t) (in place), its row sum into l_run, and O^T += V^T P~^T.
     // (The row sum stays in fp32 VALU adds: v_dot2 on the packed bf16 values
     // would halve the instruction count but does not co-execute with the
-    // matrix core.)
-    auto softmax_pv = [&](f32x16& s) {
+    // matrix core.)  With dropout the row sum is of the kept and dropped
+    // entries alike; dropped entries are then zeroed, and the 1 / (1 - p)
+    // factor is applied with the final division by the row sum.
+    const DropQuad dquad(drop_xch);
+    auto softmax_pv = [&](f32x16& s, int t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, neg_mu));
       float t8[8];
@@ -198,6 +208,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
       for (int i = 0; i < 4; ++i) t8[i] += t8[i + 4];
       l_run += (t8[0] + t8[2]) + (t8[1] + t8[3]);
+      if constexpr (DROP) {
+        // lane (l & 3) of the quad generates the block of key group (l & 3):
+        // keys key0 + 8 (l & 3) + 4 h .. +3 x the quad's four queries
+        const int gq = lane & 3;
+        const u32x4 w = philox4x32_10((uint32_t)(key0(t) + 8 * gq + 4 * h) >> 2, (uint32_t)myq >> 2,
+                                      (uint32_t)bh, 0u, a.drop_k0, a.drop_k1);
+        const u32x4 keepw = dquad.exchange(w);   // word of group g for this lane's query
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!keep_byte(keepw[r >> 2], r & 3, a.drop_t)) s[r] = 0.f;
+      }
       const PackedB pb = pack_bf16(s);
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb)
@@ -220,14 +241,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       // sub-block 2j: S(2j+1) while softmax(2j); then O += P~ V
       read_v(S0(), I0());
       scores(sb);
-      softmax_pv(sa);
+      softmax_pv(sa, 2 * j);
       read_k(S1(), I0());
       interleave_mfma_valu();
       refresh(mask_max(sb, 2 * j + 1));
       // sub-block 2j+1: S(2j+2) (next tile) while softmax(2j+1)
       read_v(S0(), I1());
       scores(sa);
-      softmax_pv(sb);
+      softmax_pv(sb, 2 * j + 1);
       read_k(S1(), I1());
       interleave_mfma_valu();
       refresh(mask_max(sa, 2 * j + 2));
@@ -251,7 +272,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
     const float l_tot = sum_halves(l_run);
     if (myq < N) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float inv = l_tot > 0.f ? (DROP ? a.drop_inv : 1.f) / l_tot : 0.f;
       bf16* orow = O + (size_t)myq * D;
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb)
@@ -281,9 +302,11 @@ struct DkdvB {
 // SPLIT (block mask present): work-groups [0, SPLIT_MAX_ITEMS) take the split
 // items of the plan (a chunk of a long column each; surplus ones exit), the
 // rest take one column each and exit if the column is split.
-template <int D, bool WALK_ONLY, bool SPLIT>
+template <int D, int MODE, bool SPLIT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_bf16_kernel(AttnArgs a) {
   using C = DkdvB<D>;
+  constexpr bool WALK_ONLY = MODE == K_WALK, DROP = MODE == K_DROP;
+  __shared__ u32x4 drop_xch[DROP ? NT : 1];
   __shared__ __attribute__((aligned(1024))) unsigned char smem[WALK_ONLY ? 16 : C::VRES + 2 * C::STAGE];
   __shared__ int cell_list[MAX_T];
   __shared__ int scratch4[4];
@@ -400,6 +423,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         // q0 + 32 qs + acc_row(r, h).  On edge tiles an entry is masked iff the
         // lane's key is at or past kv_len, or (causal) the key is past the
         // query: acc_row(r, 0) < lim.
+        u32x4 keepw;   // dropout: byte m of word g keeps query q0 + 32 qs + 8 g + 4 h + m
+        if constexpr (DROP) {
+          // lane (l & 3) of the quad (4 consecutive keys) generates the block
+          // of query group (l & 3) and turns it key-major for the exchange
+          const int gq = lane & 3;
+          const u32x4 w = philox4x32_10((uint32_t)myk >> 2, (uint32_t)(q0 + 32 * qs + 8 * gq + 4 * h) >> 2,
+                                        (uint32_t)bh, 0u, a.drop_k0, a.drop_k1);
+          keepw = DropQuad(drop_xch).exchange(byte_transpose4(w));
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int qq = 32 * qs + 8 * g + 4 * h;
@@ -409,7 +441,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * g + e;
             s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -l4[e]));
-            dp[r] = s[r] * (dp[r] - d4[e]);
+            if constexpr (DROP) {
+              // dV uses P Z (the 1 / (1 - p) factor is applied at the end);
+              // dS = P ((dO V^T) Z - delta)
+              const bool keep = keep_byte(keepw[g], e, a.drop_t);
+              dp[r] = s[r] * ((keep ? dp[r] * a.drop_inv : 0.f) - d4[e]);
+              if (!keep) s[r] = 0.f;
+            } else {
+              dp[r] = s[r] * (dp[r] - d4[e]);
+            }
           }
         }
         if (edge) {   // a masked entry has P = 0 and so dS = 0
@@ -490,7 +530,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           const int c = 32 * nb + 8 * g + 4 * h;
           store4(dkp + c, dk[nb][4 * g] * a.scale, dk[nb][4 * g + 1] * a.scale, dk[nb][4 * g + 2] * a.scale,
                  dk[nb][4 * g + 3] * a.scale);
-          store4(dvp + c, dv[nb][4 * g], dv[nb][4 * g + 1], dv[nb][4 * g + 2], dv[nb][4 * g + 3]);
+          const float vs = DROP ? a.drop_inv : 1.f;
+          store4(dvp + c, dv[nb][4 * g] * vs, dv[nb][4 * g + 1] * vs, dv[nb][4 * g + 2] * vs, dv[nb][4 * g + 3] * vs);
         }
     }
   }
@@ -507,9 +548,11 @@ struct DqB {
   static constexpr int NB = D / 32;
 };
 
-template <int D, bool WALK_ONLY>
+template <int D, int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_bf16_kernel(AttnArgs a) {
   using C = DqB<D>;
+  constexpr bool WALK_ONLY = MODE == K_WALK, DROP = MODE == K_DROP;
+  __shared__ u32x4 drop_xch[DROP ? NT : 1];
   __shared__ __attribute__((aligned(1024))) unsigned char smem[WALK_ONLY ? 16 : 2 * C::STAGE];
   __shared__ int cell_list[MAX_T];
   __shared__ int scratch4[4];
@@ -599,8 +642,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
           for (int r = 0; r < 16; ++r)
             if (acc_row(r, 0) >= lim) s[r] = 0.f;
         }
+        if constexpr (DROP) {
+          // as in the forward: lane (l & 3) generates key group (l & 3) of the
+          // quad's four queries; dS = P ((dO V^T) Z - delta)
+          const int gq = lane & 3;
+          const u32x4 w = philox4x32_10((uint32_t)(kb0 + 32 * sb + 8 * gq + 4 * h) >> 2, (uint32_t)myq >> 2,
+                                        (uint32_t)bh, 0u, a.drop_k0, a.drop_k1);
+          const u32x4 keepw = DropQuad(drop_xch).exchange(w);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - del);
+          for (int r = 0; r < 16; ++r)
+            dp[r] = s[r] * ((keep_byte(keepw[r >> 2], r & 3, a.drop_t) ? dp[r] * a.drop_inv : 0.f) - del);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - del);
+        }
         // dQ^T += K^T dS^T, K^T read transposed from the row-major tile
         const PackedB db = pack_bf16(dp);
 #pragma unroll
@@ -632,9 +687,11 @@ struct Launch;
   static hipError_t NAME(const AttnArgs& a, bool walk_only, hipStream_t s) {                            \
     const long long nwg = (long long)((a.N + CELL - 1) / CELL) * a.H * a.B;                              \
     if (walk_only)                                                                                       \
-      hipLaunchKernelGGL((KERNEL<D, true>), dim3((unsigned)nwg), dim3(NT), 0, s, a);                     \
+      hipLaunchKernelGGL((KERNEL<D, K_WALK>), dim3((unsigned)nwg), dim3(NT), 0, s, a);                   \
+    else if (a.drop_t)                                                                                   \
+      hipLaunchKernelGGL((KERNEL<D, K_DROP>), dim3((unsigned)nwg), dim3(NT), 0, s, a);                   \
     else                                                                                                 \
-      hipLaunchKernelGGL((KERNEL<D, false>), dim3((unsigned)nwg), dim3(NT), 0, s, a);                    \
+      hipLaunchKernelGGL((KERNEL<D, K_PLAIN>), dim3((unsigned)nwg), dim3(NT), 0, s, a);                  \
     return hipGetLastError();                                                                            \
   }
 
@@ -648,18 +705,22 @@ static hipError_t launch_dkdv_b(const AttnArgs& a, bool walk_only, hipStream_t s
   const long long ncol = (long long)((a.N + CELL - 1) / CELL) * a.H * a.B;
   if (!a.mask) {
     if (walk_only)
-      hipLaunchKernelGGL((dkdv_bf16_kernel<D, true, false>), dim3((unsigned)ncol), dim3(NT), 0, s, a);
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_WALK, false>), dim3((unsigned)ncol), dim3(NT), 0, s, a);
+    else if (a.drop_t)
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_DROP, false>), dim3((unsigned)ncol), dim3(NT), 0, s, a);
     else
-      hipLaunchKernelGGL((dkdv_bf16_kernel<D, false, false>), dim3((unsigned)ncol), dim3(NT), 0, s, a);
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_PLAIN, false>), dim3((unsigned)ncol), dim3(NT), 0, s, a);
     return hipGetLastError();
   }
   const hipError_t e = launch_split_plan(a, s);
   if (e != hipSuccess) return e;
   const long long nwg = SPLIT_MAX_ITEMS + ncol;
   if (walk_only)
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, true, true>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_WALK, true>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
+  else if (a.drop_t)
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_DROP, true>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, false, true>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_PLAIN, true>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -51,6 +51,9 @@ struct AttnArgs {
   const int32_t* kv_len;  // [B] or null
   uint32_t* counts;     // visit counters (walk-only instances)
   SplitWs split;        // dK/dV work split (bf16 with a block mask), else zeros
+  // dropout on P (bf16 kernels): keep iff the Philox byte >= drop_t; 0 = off
+  uint32_t drop_t, drop_k0, drop_k1;
+  float drop_inv;       // 1 / (1 - drop_t / 256)
 };
 
 // Bytes of the dK/dV split workspace for N keys and head dimension d; the

@@ -69,7 +69,7 @@ enum fa_status {
   FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE = 5, /* workspace smaller than the matching *_workspace_bytes() */
   FA_ERR_HIP = 6,       /* a HIP launch failed */
-  FA_ERR_ARG = 7        /* scale not finite and > 0, or bad selector */
+  FA_ERR_ARG = 7        /* scale not finite and > 0, bad selector, or bad dropout rate */
 };
 
 /*
@@ -164,6 +164,37 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
 int fa_debug_visits(int which, int B, int H, int N, int d, int causal,
                     const uint8_t* block_mask, const int32_t* kv_len, int dtype,
                     uint32_t* counts, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Forward and backward passes with dropout on the attention probabilities.
+ * The pages list dropout among the operations fused into the attention
+ * kernel (FlashAttention reading guide, "Ide Utama", kernel-fusion bullet)
+ * but give no formula; these entry points implement:
+ *   O = (P * Z) V,  Z_ij = keep_ij / (1 - p),  lse as without dropout,
+ * with keep_ij decided by byte (j & 3) of word (i & 3) of Philox4x32-10
+ * (Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011)
+ * with key (seed & 0xffffffff, seed >> 32) and counter
+ * (j >> 2, i >> 2, b * H + h, 0): kept iff that byte >= t, where
+ * t = round(256 * dropout_p) must be <= 255 (the effective rate is t / 256;
+ * t = 0 is no dropout).  The backward pass regenerates the same bytes from
+ * the same seed; fa_bwd_dropout must get the dropout_p and seed fa_fwd_dropout
+ * used.  Gradients: dV = (P * Z)^T dO, dP = (dO V^T) * Z,
+ * dS = P * (dP - delta), dQ = scale dS K, dK = scale dS^T Q.
+ * Errors as fa_fwd / fa_bwd, plus FA_ERR_ARG if dropout_p is not in [0, 1)
+ * or rounds to 256, and FA_ERR_DTYPE for a nonzero rate with FA_F32 (the
+ * float32 path has no dropout).  Workspace as fa_bwd.
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* block_mask, const int32_t* kv_len, int dtype,
+                   float dropout_p, uint64_t seed, void* stream);
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                   const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* block_mask, const int32_t* kv_len, int dtype,
+                   float dropout_p, uint64_t seed,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* fa_status_str(int status);

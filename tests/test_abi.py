@@ -124,6 +124,22 @@ def test_backward_validation(lib):
     assert lib.fa_bwd_preprocess(P, P, P, 1, 1, 100, 80, 0, None) == 2
 
 
+def test_dropout_validation(lib):
+    def fwd_drop(p, dtype=0, seed=1):
+        return lib.fa_fwd_dropout(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 64, 0.125, 0, None, None, dtype, p, seed,
+                                  None)
+    # checks run before any launch: a rate outside [0, 1), or one that rounds to 256/256
+    assert fwd_drop(-0.1) == 7 and fwd_drop(1.0) == 7 and fwd_drop(float("nan")) == 7
+    assert fwd_drop(0.999) == 7          # rounds to t = 256
+    assert fwd_drop(0.5, dtype=1) == 3   # the float32 path has no dropout
+    P = FAKE
+    r = lib.fa_bwd_dropout(P, P, P, P, P, P, P, P, P, 1, 1, 128, 64, 0.125, 0, None, None, 1, 0.25, 7, P, 1 << 20,
+                           None)
+    assert r == 3
+    r = lib.fa_bwd_dropout(P, P, P, P, P, P, P, P, P, 1, 1, 128, 64, 0.125, 0, None, None, 0, 2.0, 7, P, 1 << 20, None)
+    assert r == 7
+
+
 def test_debug_visits_validation(lib):
     assert lib.fa_debug_visits(3, 1, 1, 128, 64, 0, None, None, 0, FAKE, None, 0, None) == 7
     assert lib.fa_debug_visits(0, 1, 1, 128, 64, 0, None, None, 0, None, None, 0, None) == 1
