@@ -75,6 +75,53 @@ def kernel_bytes(name, B, H, N, d, esize):
             "dq": 4 * t + 2 * r + t}[name]
 
 
+def run_gpu_bench_dropout(w, steps, warmup, inp, p, seed=2024):
+    """Step with dropout on P: fa_fwd_dropout + fa_bwd_dropout (the backward's
+    stages are one call), each bracketed by HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_flashattention_amd as fa
+
+    dev = torch.device("cuda:0")
+    q, k, v, do = (torch.from_numpy(inp[n]).to(dev, torch.bfloat16) for n in ("q", "k", "v", "do"))
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bm = None if inp.get("block_mask") is None else torch.from_numpy(np.ascontiguousarray(inp["block_mask"])).to(dev)
+    kl = None if inp.get("kv_len") is None else torch.from_numpy(inp["kv_len"].astype(np.int32)).to(dev)
+    ws = torch.empty(max(fa.fa_bwd_workspace_bytes(B, H, N, d, fa.FA_BF16, bm is not None), 256),
+                     dtype=torch.uint8, device=dev)
+    kw = dict(scale=w.scale, causal=w.causal, block_mask=bm, kv_len=kl, dropout_p=p, seed=seed)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        fa.fa_fwd(q, k, v, o, lse, stream=stream, **kw)
+        if ev:
+            ev[1].record(stream)
+        fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, workspace=ws, stream=stream, **kw)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    per = {"fwd": sum(e[0].elapsed_time(e[1]) for e in evs) / steps,
+           "bwd": sum(e[1].elapsed_time(e[2]) for e in evs) / steps}
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(dq).all())
+    return start.elapsed_time(end) / steps, per, (B, H, N, d)
+
+
 def run_gpu_bench(w, steps, warmup, inp):
     import numpy as np
     import torch
@@ -290,6 +337,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4, choices=(1, 2, 3, 4, 5),
                     help="workload to time (default 4, the long-context line)")
     ap.add_argument("--sweep", action="store_true", help="time the N = 1K..16K sweep (one JSON line per shape)")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="time the step with dropout on P at this rate (fa_fwd_dropout + fa_bwd_dropout)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg (profiling runs)")
     ap.add_argument("--cpu-baseline", action="store_true", help="run the CPU oracle leg for --workload other than 4")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -312,6 +361,21 @@ def main():
     from workloads import WORKLOADS, digest, make_inputs
     w = WORKLOADS[args.workload]
     inp = make_inputs(w)
+    if args.dropout:
+        step_ms, per, (B, H, N, d) = run_gpu_bench_dropout(w, args.steps, args.warmup, inp, args.dropout)
+        F = workload_fwd_flops(w, inp)
+        t = round(args.dropout * 256)
+        print(json.dumps({
+            "metric": METRIC, "value": round(3.5 * F / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": f"synthetic (seeded N(0, {w.sigma ** 2:g}) Q/K/V/dO, inputs resident in HBM)",
+            "config": {"workload": f"workload {args.workload} with dropout p = {t}/256 on P", "B": B, "H": H,
+                       "N": N, "d": d, "causal": w.causal},
+            "kernel_ms": {n: round(x, 4) for n, x in per.items()},
+            "fwd_tflops": round(F / (per["fwd"] * 1e-3) / 1e12, 2),
+            "bwd_tflops": round(2.5 * F / (per["bwd"] * 1e-3) / 1e12, 2)}), flush=True)
+        return
     if args.copy_calibration:
         copy_calibration()
     step_ms, per, wall, (B, H, N, d) = run_gpu_bench(w, args.steps, args.warmup, inp)
