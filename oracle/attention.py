@@ -31,10 +31,13 @@ import numpy as np
 CELL = 128
 
 
-def allowed(rows, nk, causal=False, block_mask=None, kv_len=None, cell=CELL, keys=None):
+def allowed(rows, nk, causal=False, block_mask=None, kv_len=None, cell=CELL, keys=None, causal_offset=0):
     """Boolean [len(rows), nk]; True where key j may be attended by query i.
 
-    causal: j <= i (queries and keys share positions, top-left aligned).
+    causal: j <= i + causal_offset.  With as many queries as keys the offset
+    is 0 (queries and keys share positions, top-left aligned); for Nq queries
+    against Nk >= Nq keys it is Nk - Nq, the queries being the last Nq
+    positions (bottom-right aligned).
     kv_len: j < kv_len (key padding).
     block_mask: block_mask[i // cell, j // cell] == 1 (block-sparse cells,
     FlashAttention reading guide "Ekstensi: Block-Sparse FlashAttention").
@@ -45,7 +48,7 @@ def allowed(rows, nk, causal=False, block_mask=None, kv_len=None, cell=CELL, key
     nk = j.shape[1]
     ok = np.ones((i.shape[0], nk), dtype=bool)
     if causal:
-        ok &= j <= i
+        ok &= j <= i + int(causal_offset)
     if kv_len is not None:
         ok &= j < int(kv_len)
     if block_mask is not None:
@@ -66,14 +69,14 @@ def _probs(Sm):
     return P, lse
 
 
-def head_forward(Q, K, V, scale, rows=None, causal=False, block_mask=None, kv_len=None):
-    """One (b, h): O[rows], lse[rows] with Q, K, V as [N, d] arrays."""
+def head_forward(Q, K, V, scale, rows=None, causal=False, block_mask=None, kv_len=None, causal_offset=0):
+    """One (b, h): O[rows], lse[rows] with Q [Nq, d] and K, V [Nk, d]."""
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
     rows = np.arange(Q.shape[0]) if rows is None else np.asarray(rows)
     S = scale * (Q[rows] @ K.T)
-    S = np.where(allowed(rows, K.shape[0], causal, block_mask, kv_len), S, -np.inf)
+    S = np.where(allowed(rows, K.shape[0], causal, block_mask, kv_len, causal_offset=causal_offset), S, -np.inf)
     P, lse = _probs(S)
     return P @ V, lse
 

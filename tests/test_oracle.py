@@ -272,3 +272,56 @@ def test_expected_visits_hand_enumerated():
     assert ev[0].tolist() == [[1, 0, 0]] * 3
     ev = visits.expected_visits(1, 1, causal=True)
     assert ev.tolist() == [[[1]]]
+
+
+# ---------------------------------------------------------------- fewer queries than keys
+
+def test_bottom_right_causal_by_brute_force():
+    """Nq queries against Nk >= Nq keys, causal with the queries as the last Nq
+    positions: query i may see key j iff j <= i + (Nk - Nq).  Pure-Python loops."""
+    import math
+    rng = np.random.Generator(np.random.PCG64(60))
+    Nq, Nk, d, scale = 5, 9, 3, 0.7
+    Q, K, V = rng.standard_normal((Nq, d)), rng.standard_normal((Nk, d)), rng.standard_normal((Nk, d))
+    O, lse = attention.head_forward(Q, K, V, scale, causal=True, causal_offset=Nk - Nq)
+    for i in range(Nq):
+        keys = [j for j in range(Nk) if j <= i + Nk - Nq]
+        s = [scale * sum(Q[i, t] * K[j, t] for t in range(d)) for j in keys]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        den = sum(w)
+        for t in range(d):
+            assert abs(O[i, t] - sum(wj * V[j, t] for wj, j in zip(w, keys)) / den) < 1e-12
+        assert abs(lse[i] - (m + math.log(den))) < 1e-12
+    # with as many queries as keys the offset is zero and this is the top-left causal mask
+    O1, _ = attention.head_forward(Q, K[:Nq], V[:Nq], scale, causal=True, causal_offset=0)
+    O2, _ = attention.head_forward(Q, K[:Nq], V[:Nq], scale, causal=True)
+    assert np.array_equal(O1, O2)
+
+
+def test_key_splits_merge_to_the_full_softmax():
+    """Splitting the keys into contiguous ranges and combining the per-range
+    (m, l, O) with the pages' two-block merge gives the full result (what a
+    split-key forward relies on)."""
+    rng = np.random.Generator(np.random.PCG64(61))
+    Nq, Nk, d, scale = 7, 50, 4, 0.5
+    Q, K, V = rng.standard_normal((Nq, d)), rng.standard_normal((Nk, d)), rng.standard_normal((Nk, d))
+    O, lse = attention.head_forward(Q, K, V, scale, causal=True, causal_offset=Nk - Nq)
+    ok = attention.allowed(np.arange(Nq), Nk, causal=True, causal_offset=Nk - Nq)
+    m_run = np.full(Nq, -np.inf)
+    l_run = np.zeros(Nq)
+    acc = np.zeros((Nq, d))
+    for lo, hi in ((0, 13), (13, 31), (31, 50)):
+        S = np.where(ok[:, lo:hi], scale * Q @ K[lo:hi].T, -np.inf)
+        m_b = S.max(axis=1)
+        live = np.isfinite(m_b)
+        E = np.where(live[:, None], np.exp(S - np.where(live, m_b, 0.0)[:, None]), 0.0)
+        l_b = E.sum(axis=1)
+        o_b = E @ V[lo:hi]                                   # unnormalised block output
+        m_new, l_new = online.merge(m_run, l_run, m_b, l_b)
+        wa = np.where(np.isfinite(m_run), np.exp(m_run - m_new), 0.0)
+        wb = np.where(live, np.exp(m_b - m_new), 0.0)
+        acc = wa[:, None] * acc + wb[:, None] * o_b
+        m_run, l_run = m_new, l_new
+    assert np.allclose(acc / l_run[:, None], O, rtol=1e-12, atol=1e-12)
+    assert np.allclose(m_run + np.log(l_run), lse, rtol=1e-12, atol=1e-12)
