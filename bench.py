@@ -183,6 +183,85 @@ def run_gpu_bench(w, steps, warmup, inp):
     return total_ms / steps, per, wall, (B, H, N, d)
 
 
+def splitkv_pairs(Nq, Nk, causal):
+    """Allowed (query, key) pairs of one head: all Nq Nk, or under the causal
+    mask aligned to the last Nq keys (j <= i + Nk - Nq) sum_i min(Nk, i + Nk - Nq + 1)."""
+    if not causal:
+        return Nq * Nk
+    return sum(max(0, min(Nk, i + Nk - Nq + 1)) for i in range(Nq))
+
+
+def splitkv_alg(w):
+    """Algorithmic flops (S and PV products over allowed pairs) and compulsory
+    HBM bytes (Q, K, V read once; O and lse written once) of one split-key
+    forward call."""
+    B, H, Nq, Nk, d = w["B"], w["H"], w["Nq"], w["Nk"], w["d"]
+    flops = 4.0 * B * H * splitkv_pairs(Nq, Nk, w["causal"]) * d
+    nbytes = 2 * B * H * (2 * Nq + 2 * Nk) * d + 4 * B * H * Nq
+    return flops, nbytes
+
+
+def run_gpu_bench_splitkv(which, steps, warmup):
+    """One step = one fa_fwd_splitkv call (range kernel + merge), bracketed by
+    HIP events on the launch stream."""
+    import torch
+
+    import exact_io_aware_flashattention_amd as fa
+    from workloads import SPLITKV_WORKLOADS, draw_split_qkv, digest
+
+    w = SPLITKV_WORKLOADS[which]
+    B, H, Nq, Nk, d = w["B"], w["H"], w["Nq"], w["Nk"], w["d"]
+    qa, ka, va = draw_split_qkv(B, H, Nq, Nk, d, w["sigma"], w["seed"])
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(a).to(dev, torch.bfloat16) for a in (qa, ka, va))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    scale = 1.0 / math.sqrt(d)
+
+    def step():
+        fa.fa_fwd_splitkv(q, k, v, o, lse, scale=scale, causal=w["causal"], workspace=ws, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all())
+    call_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    flops, nbytes = splitkv_alg(w)
+    nsplit = fa.fa_fwd_splitkv_num_splits(B, H, Nq, Nk, 0)
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    tf, gbs = flops / (call_ms * 1e-3) / 1e12, nbytes / (call_ms * 1e-3) / 1e9
+    if flops / nbytes > ridge:
+        metric, value, unit = "split-key forward TFLOP/s (bf16, 1 GPU)", tf, "TFLOP/s"
+        roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    else:
+        metric, value, unit = "split-key forward GB/s of compulsory HBM traffic (bf16, 1 GPU)", gbs, "GB/s"
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roofline.update({"kernel": "fa_fwd_splitkv call (range kernel + merge)", "traffic": None,
+                     "alg_flops": flops, "alg_bytes": nbytes})
+    return {
+        "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(start.elapsed_time(end) / steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": f"synthetic (seeded N(0, {w['sigma'] ** 2:g}) Q/K/V, inputs resident in HBM)",
+        "config": {"workload": w["desc"], "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "causal": w["causal"],
+                   "num_splits": nsplit, "input_sha256": digest(qa, ka, va)},
+        "call_ms": round(call_ms, 4), "tflops": round(tf, 2), "hbm_gbs": round(gbs, 1),
+        "roofline": roofline}
+
+
 COPY_BYTES = 256 << 20
 
 
@@ -221,8 +300,8 @@ def cpu_baseline(w, inp, heads=2):
 
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "long_context_hbm_traffic.txt")
-KERNEL_SYMBOL = {"fwd": "fwd_bf16_kernel<128, false>", "dkdv": "dkdv_bf16_kernel<128, false, false>",
-                 "dq": "dq_bf16_kernel<128, false>", "pre": "bwd_pre_kernel"}
+KERNEL_SYMBOL = {"fwd": "fwd_bf16_kernel<128, 0>", "dkdv": "dkdv_bf16_kernel<128, 0, false>",
+                 "dq": "dq_bf16_kernel<128, 0>", "pre": "bwd_pre_kernel"}
 
 
 def kernel_source_hash():
@@ -339,6 +418,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="time the N = 1K..16K sweep (one JSON line per shape)")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="time the step with dropout on P at this rate (fa_fwd_dropout + fa_bwd_dropout)")
+    ap.add_argument("--splitkv", choices=("decode", "prefill"),
+                    help="time the split-key forward (fa_fwd_splitkv) on a decode or chunked-prefill shape")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg (profiling runs)")
     ap.add_argument("--cpu-baseline", action="store_true", help="run the CPU oracle leg for --workload other than 4")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -356,6 +437,9 @@ def main():
 
     if args.sweep:
         sweep(args.steps, args.warmup)
+        return
+    if args.splitkv:
+        print(json.dumps(run_gpu_bench_splitkv(args.splitkv, args.steps, args.warmup)), flush=True)
         return
 
     from workloads import WORKLOADS, digest, make_inputs

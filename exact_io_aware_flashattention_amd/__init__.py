@@ -22,7 +22,8 @@ WALK_FWD, WALK_DKDV, WALK_DQ = 0, 1, 2
 CELL = 128
 
 EXPORTS = ("fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd_dkdv_workspace_bytes", "fa_bwd", "fa_bwd_preprocess",
-           "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_dropout", "fa_bwd_dropout", "fa_debug_visits", "fa_status_str")
+           "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_splitkv_workspace_bytes",
+           "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv", "fa_debug_visits", "fa_status_str")
 
 
 class FAError(RuntimeError):
@@ -58,6 +59,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fa_bwd_dq": [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, P],
         "fa_fwd_dropout": [P, P, P, P, P, I, I, I, I, F, I, P, P, I, F, U64, P],
         "fa_bwd_dropout": [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, F, U64, P, S, P],
+        "fa_fwd_splitkv_workspace_bytes": [I, I, I, I, I, I],
+        "fa_fwd_splitkv_num_splits": [I, I, I, I, I],
+        "fa_fwd_splitkv": [P, P, P, P, P, I, I, I, I, I, F, I, P, I, I, P, S, P],
         "fa_debug_visits": [I, I, I, I, I, I, P, P, I, P, P, S, P],
         "fa_status_str": [I],
     }
@@ -67,6 +71,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_dkdv_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_str.restype = ctypes.c_char_p
     _lib = lib
     return lib
@@ -168,6 +173,37 @@ def _workspace(workspace, need, device):
     if workspace is None:
         return None, 0
     return workspace, workspace.numel() * workspace.element_size()
+
+
+def fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits=0) -> int:
+    return int(load_library().fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits))
+
+
+def fa_fwd_splitkv_num_splits(B, H, Nq, Nk, num_splits=0) -> int:
+    return int(load_library().fa_fwd_splitkv_num_splits(B, H, Nq, Nk, num_splits))
+
+
+def fa_fwd_splitkv(q, k, v, o=None, lse=None, *, scale=None, causal=False, kv_len=None, num_splits=0,
+                   workspace=None, stream=None):
+    """O, lse for Nq queries [B,H,Nq,d] against Nk keys k, v [B,H,Nk,d] (bf16),
+    with the keys split over num_splits ranges (0 = chosen from the sizes)
+    whose partial results are merged.  causal aligns the queries with the
+    last Nq key positions (key j allowed for query i iff j <= i + Nk - Nq)."""
+    import torch
+    B, H, Nq, d = _shape(q)
+    Bk, Hk, Nk, dk = _shape(k)
+    if (Bk, Hk, dk) != (B, H, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_like(q, q, k, v, o, lse, kv_len)
+    ws, nbytes = _workspace(workspace, fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits), q.device)
+    _call("fa_fwd_splitkv", _ptr(q), _ptr(k) if Nk else None, _ptr(v) if Nk else None, _ptr(o), _ptr(lse), B, H,
+          Nq, Nk, d, _scale(scale, d), int(bool(causal)), _ptr(kv_len), _dtype_code(q), int(num_splits), _ptr(ws),
+          nbytes, _stream(stream))
+    return o, lse
 
 
 def fa_bwd(q, k, v, o, dO, lse, dq=None, dk=None, dv=None, *, scale=None, causal=False, block_mask=None,

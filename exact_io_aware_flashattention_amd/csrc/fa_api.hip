@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fa.h"
 #include "fa_kernels.hpp"
 
@@ -238,6 +240,70 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   return dq_impl(q, k, v, dO, lse, delta, dq, B, H, N, d, scale, causal, block_mask, kv_len, dtype, drop, stream);
 }
 
+// Key ranges of a split-key forward: nsplit ranges of tps 64-key tiles each.
+// Few queries (Nq <= kDecodeMaxQ) take the decoding kernel: one wave per
+// (range, b, h), ranges of whole tiles.  Otherwise one 256-thread work-group
+// per (range, b, h, 128 queries), ranges of whole 128-key cells (tps even).
+// num_splits = 0 picks the largest count that keeps every unit of work
+// resident at once -- 256 compute units, each holding two work-groups of the
+// attention kernel: the ranges are of equal length, so a second, partly
+// filled round would cost as much as the first.  Decoding waves are capped
+// at one per SIMD (1024): measured on this part, more concurrent read
+// streams lower the bandwidth they reach together.
+constexpr int kSplitKvMax = 1024;
+constexpr int kDecodeMaxQ = 4;
+constexpr long long kResidentGroups = 256 * 2;
+constexpr long long kResidentWaves = 256 * 4;
+
+struct KvPlan {
+  int nsplit, tps;
+  bool decode;
+};
+
+int splitkv_plan(int B, int H, int Nq, int Nk, int num_splits, KvPlan* p) {
+  if (num_splits < 0 || num_splits > kSplitKvMax) return FA_ERR_ARG;
+  p->decode = Nq <= kDecodeMaxQ;
+  const long long Tq = (Nq + kCell - 1) / kCell;
+  const long long tiles = (Nk + 63) / 64;
+  const long long unit = p->decode ? 1 : 2;   // tiles per range step
+  const long long groups = p->decode ? (long long)B * H : Tq * B * H;
+  const long long slots = p->decode ? kResidentWaves : kResidentGroups;
+  long long want = num_splits;
+  if (want == 0) want = groups > 0 ? slots / groups : 1;
+  want = std::max(1LL, std::min<long long>(want, kSplitKvMax));
+  long long tps = (tiles + want - 1) / want;
+  tps = std::max(unit, (tps + unit - 1) / unit * unit);
+  p->tps = (int)tps;
+  p->nsplit = (int)std::max(1LL, (tiles + tps - 1) / tps);
+  // the launch runs groups * nsplit work-groups (waves, when decoding) of 256
+  if (groups * p->nsplit >= (1LL << 32) / fa::NT_HOST) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_splitkv_shape(int B, int H, int Nq, int Nk, int d, int dtype, bool* empty) {
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_DTYPE;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_SHAPE;
+  *empty = (B == 0 || H == 0 || Nq == 0);
+  if (*empty) return FA_OK;
+  if (dtype != FA_BF16) return FA_ERR_DTYPE;
+  if ((long long)B * H * Nq * (d / 4) >= (1LL << 32) - fa::NT_HOST) return FA_ERR_SHAPE;
+  if ((long long)Nq * d > 0x7fffffffLL || (long long)Nk * d > 0x7fffffffLL) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+size_t splitkv_o_bytes(int B, int H, int Nq, int d, int nsplit) {
+  return (size_t)nsplit * B * H * Nq * d * sizeof(float);
+}
+
+size_t splitkv_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  bool empty = false;
+  KvPlan p;
+  if (check_splitkv_shape(B, H, Nq, Nk, d, FA_BF16, &empty) != FA_OK || empty) return 0;
+  if (splitkv_plan(B, H, Nq, Nk, num_splits, &p) != FA_OK) return 0;
+  return splitkv_o_bytes(B, H, Nq, d, p.nsplit) + (size_t)p.nsplit * B * H * Nq * 2 * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -314,6 +380,50 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
   FA_TRY(make_drop(dropout_p, seed, dtype, &drop));
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, scale, causal, block_mask, kv_len, dtype, drop,
                   workspace, workspace_bytes, stream);
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  return splitkv_bytes(B, H, Nq, Nk, d, num_splits);
+}
+
+int fa_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int num_splits) {
+  KvPlan p;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk < 0) return 0;
+  if (splitkv_plan(B, H, Nq, Nk, num_splits, &p) != FA_OK) return 0;
+  return p.nsplit;
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                   int d, float scale, int causal, const int32_t* kv_len, int dtype, int num_splits,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  FA_TRY(check_splitkv_shape(B, H, Nq, Nk, d, dtype, &empty));
+  if (empty) return FA_OK;
+  KvPlan p;
+  FA_TRY(splitkv_plan(B, H, Nq, Nk, num_splits, &p));
+  FA_TRY(check_tensors({q, o}));
+  if (Nk > 0) FA_TRY(check_tensors({k, v}));
+  FA_TRY(check_rowstats({lse}));
+  FA_TRY(check_masks(nullptr, kv_len));
+  FA_TRY(check_scale(scale));
+  if (!workspace) return FA_ERR_NULL;
+  if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+  if (workspace_bytes < splitkv_bytes(B, H, Nq, Nk, d, num_splits)) return FA_ERR_WORKSPACE;
+  fa::AttnArgs a = make_args(Shape{B, H, Nq, d, dtype}, scale, causal, nullptr, kv_len);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out0 = o;
+  a.lse = lse;
+  a.Nk = Nk;
+  a.causal_off = Nk - Nq;
+  a.nsplit = p.nsplit;
+  a.split_tiles = p.tps;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                       splitkv_o_bytes(B, H, Nq, d, p.nsplit));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(p.decode ? fa::launch_fwd_decode_bf16(a, d, st) : fa::launch_fwd_splitkv_bf16(a, d, st));
 }
 
 int fa_debug_visits(int which, int B, int H, int N, int d, int causal, const uint8_t* block_mask,

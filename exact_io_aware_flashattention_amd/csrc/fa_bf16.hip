@@ -29,7 +29,7 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 *
 
 // Kernel instances: the attention arithmetic, the tile walk alone (visit
 // counters), or the arithmetic with dropout on P.
-constexpr int K_PLAIN = 0, K_WALK = 1, K_DROP = 2;
+constexpr int K_PLAIN = 0, K_WALK = 1, K_DROP = 2, K_SPLITKV = 3;
 
 // Scheduling hint for a branch-free region holding 16 MFMAs and the VALU work
 // of one 32-key sub-block: alternate one MFMA with up to six VALU
@@ -78,26 +78,42 @@ struct FwdB {
 template <int D, int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(AttnArgs a) {
   using C = FwdB<D>;
-  constexpr bool WALK_ONLY = MODE == K_WALK, DROP = MODE == K_DROP;
+  constexpr bool WALK_ONLY = MODE == K_WALK, DROP = MODE == K_DROP, SPLITKV = MODE == K_SPLITKV;
   __shared__ u32x4 drop_xch[DROP ? NT : 1];
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf[WALK_ONLY ? 16 : 2 * C::TILE];
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf[WALK_ONLY ? 16 : 2 * C::TILE];
   __shared__ int cell_list[MAX_T];
   __shared__ int scratch4[4];
 
-  const int N = a.N;
+  const int N = a.N;                       // queries (and keys, unless SPLITKV)
+  const int NK = SPLITKV ? a.Nk : N;       // keys
+  const int off = SPLITKV ? a.causal_off : 0;   // causal: key <= query + off
   const int T_cells = (N + CELL - 1) / CELL;
-  const WorkUnit u = work_unit(blockIdx.x, gridDim.x, a.B * a.H, T_cells, a.causal);
-  const int bh = u.bh;
-  const int qi = a.causal ? T_cells - 1 - u.t : u.t;   // heaviest causal rows first
+  int bh, qi, split = 0;
+  if constexpr (SPLITKV) {
+    // work-group = (key range, head, query cell): ranges fastest, then heads,
+    // then query cells, heaviest (last) causal cells first as in the plain
+    // forward; the work-groups of one (head, range) sit nsplit * B * H apart.
+    split = blockIdx.x % a.nsplit;
+    const int L = blockIdx.x / a.nsplit, BH = a.B * a.H;
+    const int t = L / BH;
+    bh = L - t * BH;
+    qi = a.causal ? T_cells - 1 - t : t;
+  } else {
+    const WorkUnit u = work_unit(blockIdx.x, gridDim.x, a.B * a.H, T_cells, a.causal);
+    bh = u.bh;
+    qi = a.causal ? T_cells - 1 - u.t : u.t;   // heaviest causal rows first
+  }
   const int b = bh / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
 
-  const int kvl = clamp_kv_len(a, b);
+  const int kvl = SPLITKV ? (a.kv_len ? min(max(a.kv_len[b], 0), NK) : NK) : clamp_kv_len(a, b);
   const int q_lo = qi * CELL, q_hi = min(q_lo + CELL, N);
-  const int kv_end = a.causal ? min(kvl, q_hi) : kvl;
-  const Walk walk = row_walk(a, qi, kv_end, T_cells, cell_list, scratch4, 6);
+  const int kv_end = a.causal ? min(kvl, q_hi + off) : kvl;
+  const Walk walk = SPLITKV ? range_walk(split * a.split_tiles,
+                                         min((kv_end + 63) >> 6, (split + 1) * a.split_tiles) - split * a.split_tiles)
+                            : row_walk(a, qi, kv_end, T_cells, cell_list, scratch4, 6);
 
   if constexpr (WALK_ONLY) {
     for (int it = 0; it < walk.ntiles; ++it)
@@ -105,16 +121,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         atomicAdd(&a.counts[((size_t)b * T_cells + qi) * T_cells + walk.cell(it >> 1)], 1u);
     return;
   } else {
-    const size_t head = (size_t)bh * N * D;
+    const size_t head = (size_t)bh * N * D, khead = (size_t)bh * NK * D;
     const bf16* Q = reinterpret_cast<const bf16*>(a.q) + head;
-    bf16* O = reinterpret_cast<bf16*>(a.out0) + head;
-    const bf16* Kh = reinterpret_cast<const bf16*>(a.k) + head;
-    const bf16* Vh = reinterpret_cast<const bf16*>(a.v) + head;
+    const bf16* Kh = reinterpret_cast<const bf16*>(a.k) + khead;
+    const bf16* Vh = reinterpret_cast<const bf16*>(a.v) + khead;
     const TileDma<D, 64> dma;
 
     const int qw0 = q_lo + wave * 32;
     const int myq = qw0 + l32;
     const int ntiles = walk.ntiles, nsub = 2 * ntiles;
+    // With few queries (decode) most waves of a split-key work-group hold no
+    // query row: they still move their share of every tile but skip the math.
+    const bool live = !SPLITKV || qw0 < N;
 
     u32x4 qf[C::SSTEPS];
 #pragma unroll
@@ -130,8 +148,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     float m_run = neg_inf(), l_run = 0.f, neg_mu = 0.f, thr = neg_inf();
     const float inv_c = 1.f / a.c;
 
-    auto issue_k = [&](int j) { dma.load(Kh, N, walk.tile_start(j), kbuf + (j & 1) * C::TILE); };
-    auto issue_v = [&](int j) { dma.load(Vh, N, walk.tile_start(j), vbuf + (j & 1) * C::TILE); };
+    auto issue_k = [&](int j) { dma.load(Kh, NK, walk.tile_start(j), kbuf + (j & 1) * C::TILE); };
+    auto issue_v = [&](int j) { dma.load(Vh, NK, walk.tile_start(j), vbuf + (j & 1) * C::TILE); };
     auto key0 = [&](int t) { return walk.tile_start(t >> 1) + 32 * (t & 1); };
 
     u32x4 kfrag[C::SSTEPS];          // K rows of one sub-block: row l32, chunk 2 st + h
@@ -164,8 +182,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     auto mask_max = [&](f32x16& s, int t) -> float {
       if (t >= nsub) return neg_inf();
       const int k0 = key0(t);
-      if ((k0 + 32 > kvl) || (a.causal && k0 + 31 > qw0)) {
-        const int lim = min(kvl, a.causal ? myq + 1 : kvl) - k0 - 4 * h;
+      if ((k0 + 32 > kvl) || (a.causal && k0 + 31 > qw0 + off)) {
+        const int lim = min(kvl, a.causal ? myq + 1 + off : kvl) - k0 - 4 * h;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (acc_row(r, 0) >= lim) s[r] = neg_inf();
@@ -238,6 +256,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       __syncthreads();
       if (j + 2 < ntiles) issue_k(j + 2);
       if (j + 1 < ntiles) issue_v(j + 1);
+      if (!live) return;
       // sub-block 2j: S(2j+1) while softmax(2j); then O += P~ V
       read_v(S0(), I0());
       scores(sb);
@@ -260,10 +279,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       if (ntiles > 1) issue_k(1);
       wait_loads();
       __syncthreads();
-      read_k(I0(), I0());
-      scores(sa);
-      read_k(I0(), I1());
-      refresh(mask_max(sa, 0));
+      if (live) {
+        read_k(I0(), I0());
+        scores(sa);
+        read_k(I0(), I1());
+        refresh(mask_max(sa, 0));
+      }
       for (int j = 0; j < ntiles; j += 2) {
         tile_step(I0(), j);
         if (j + 1 < ntiles) tile_step(I1(), j + 1);
@@ -271,9 +292,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     }
 
     const float l_tot = sum_halves(l_run);
+    if constexpr (SPLITKV) {
+      // partial result of this key range: unnormalised O (relative to m_run)
+      // and (m_run in log2 units, l); the merge kernel combines the ranges
+      if (myq < N) {
+        const size_t prow = ((size_t)split * a.B * a.H + bh) * N + myq;
+        float* po = a.part_o + prow * D;
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<f32x4*>(po + 32 * nb + 8 * g + 4 * h) =
+                f32x4{acc[nb][4 * g], acc[nb][4 * g + 1], acc[nb][4 * g + 2], acc[nb][4 * g + 3]};
+        if (h == 0) *reinterpret_cast<float2*>(a.part_ml + 2 * prow) = float2{m_run, l_tot};
+      }
+      return;
+    }
     if (myq < N) {
       const float inv = l_tot > 0.f ? (DROP ? a.drop_inv : 1.f) / l_tot : 0.f;
-      bf16* orow = O + (size_t)myq * D;
+      bf16* orow = reinterpret_cast<bf16*>(a.out0) + head + (size_t)myq * D;
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
@@ -722,6 +759,63 @@ static hipError_t launch_dkdv_b(const AttnArgs& a, bool walk_only, hipStream_t s
   else
     hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_PLAIN, true>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
   return hipGetLastError();
+}
+
+// Merge of the key ranges of a split-key forward (one thread per row and four
+// output features): m = max_s m_s, w_s = 2^(m_s - m), l = sum_s w_s l_s,
+// O = sum_s w_s O_s / l, lse = (m + log2 l) ln 2 -- the two-block combination
+// of the incremental softmax (FlashAttention reading guide, "Pelacakan
+// Softmax Inkremental"), applied across ranges.  A range without keys has
+// m = -inf and l = 0 and gets weight 0.
+template <int D>
+__global__ __launch_bounds__(NT) void splitkv_merge_kernel(AttnArgs a) {
+  const long long rows = (long long)a.B * a.H * a.N;
+  const long long idx = (long long)blockIdx.x * NT + threadIdx.x;
+  const long long row = idx / (D / 4);
+  const int g = (int)(idx - row * (D / 4));
+  if (row >= rows) return;
+  float m = neg_inf();
+  for (int s = 0; s < a.nsplit; ++s) m = fmaxf(m, a.part_ml[2 * (s * rows + row)]);
+  float l = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float ms = a.part_ml[2 * (s * rows + row)];
+    if (ms == neg_inf()) continue;
+    const float w = __builtin_amdgcn_exp2f(ms - m);
+    l += w * a.part_ml[2 * (s * rows + row) + 1];
+    const f32x4 x = *reinterpret_cast<const f32x4*>(a.part_o + (s * rows + row) * D + 4 * g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] += w * x[e];
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  bf16* orow = reinterpret_cast<bf16*>(a.out0) + row * D + 4 * g;
+  store4(orow, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+  if (g == 0) a.lse[row] = l > 0.f ? (m + __log2f(l)) * LN2 : neg_inf();
+}
+
+hipError_t launch_splitkv_merge(const AttnArgs& a, int d, hipStream_t s) {
+  const long long threads = (long long)a.B * a.H * a.N * (d / 4);
+  const dim3 grid((unsigned)((threads + NT - 1) / NT));
+  if (d == 64)
+    hipLaunchKernelGGL((splitkv_merge_kernel<64>), grid, dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((splitkv_merge_kernel<128>), grid, dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_splitkv_b(const AttnArgs& a, hipStream_t s) {
+  const long long nwg = (long long)((a.N + CELL - 1) / CELL) * a.H * a.B * a.nsplit;
+  if (nwg > 0) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, K_SPLITKV>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_splitkv_merge(a, D, s);
+}
+
+hipError_t launch_fwd_splitkv_bf16(const AttnArgs& a, int d, hipStream_t s) {
+  return d == 64 ? launch_splitkv_b<64>(a, s) : launch_splitkv_b<128>(a, s);
 }
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s) {

@@ -54,6 +54,12 @@ struct AttnArgs {
   // dropout on P (bf16 kernels): keep iff the Philox byte >= drop_t; 0 = off
   uint32_t drop_t, drop_k0, drop_k1;
   float drop_inv;       // 1 / (1 - drop_t / 256)
+  // split-key forward (N = queries): Nk keys, causal limit key <= query +
+  // causal_off, nsplit key ranges of split_tiles 64-key tiles each; partial
+  // outputs part_o [nsplit][B*H*N][d] and (m, l) part_ml [nsplit][B*H*N][2]
+  int Nk, causal_off, nsplit, split_tiles;
+  float* part_o;
+  float* part_ml;
 };
 
 // Bytes of the dK/dV split workspace for N keys and head dimension d; the
@@ -73,5 +79,11 @@ hipError_t launch_dkdv_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_
 hipError_t launch_dq_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s);
 // Column counts + plan of the dK/dV split (needs a.mask and a.split).
 hipError_t launch_split_plan(const AttnArgs& a, hipStream_t s);
+// Split-key forward (bf16): partial outputs of every key range, then their merge.
+hipError_t launch_fwd_splitkv_bf16(const AttnArgs& a, int d, hipStream_t s);
+// The same for at most four queries per head (one wave per key range).
+hipError_t launch_fwd_decode_bf16(const AttnArgs& a, int d, hipStream_t s);
+// Merge of the partial outputs a.part_o / a.part_ml into a.out0 and a.lse.
+hipError_t launch_splitkv_merge(const AttnArgs& a, int d, hipStream_t s);
 
 }  // namespace fa

@@ -93,6 +93,18 @@ __device__ inline Walk col_walk(const AttnArgs& a, int kj, int kvl, int T, int* 
   return w;
 }
 
+// Walk of one key range of a split-key forward: 64-key tiles [t0, t0 + n)
+// (t0 even, so the range starts on a 128-key cell).
+__device__ inline Walk range_walk(int t0, int n) {
+  Walk w;
+  w.base = t0 >> 1;
+  w.tsh = 6;
+  w.list = nullptr;
+  w.ntiles = max(n, 0);
+  w.ncells = (w.ntiles + 1) >> 1;
+  return w;
+}
+
 // Restrict a block-sparse walk to its visited cells [c0, c0 + cnt) (one chunk
 // of a split column).
 __device__ inline void take_chunk(Walk& w, int c0, int cnt, int limit) {

@@ -196,6 +196,49 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
                    float dropout_p, uint64_t seed,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Split-key forward for few queries against many keys (decoding, chunked
+ * prefill).  The pages motivate splitting attention along the sequence when
+ * batch x heads alone cannot fill the device (datacamp "Penjelasan Flash
+ * Attention", Flash Attention 2, "Paralelisme sepanjang panjang sekuens").
+ * Here the keys of each (b, h) are cut into num_splits contiguous ranges;
+ * each range runs the forward pass's incremental softmax over its keys and
+ * writes an unnormalised float32 partial output with its row statistics
+ * (m, l); a second kernel combines the ranges of every row with the
+ * two-block rule of the incremental softmax (FlashAttention reading guide,
+ * "Pelacakan Softmax Inkremental": m = max m_s, l = sum_s e^{m_s - m} l_s,
+ * O = sum_s e^{m_s - m} O_s / l).  With Nq <= 4 one wave handles a range of
+ * one (b, h) (a bandwidth-bound kernel, ranges of whole 64-key tiles);
+ * otherwise one work-group handles a range for 128 queries of one (b, h)
+ * (the matrix-core forward kernel, ranges of whole 128-key cells).
+ *   q, o     [B,H,Nq,d] bf16;  k, v  [B,H,Nk,d] bf16;  lse [B,H,Nq] float32.
+ *   causal   nonzero: queries are the last Nq of Nk positions, so key j is
+ *            allowed for query i iff j <= i + Nk - Nq (for Nk = Nq this is
+ *            fa_fwd's mask; queries with i + Nk - Nq < 0 have no key).
+ *   kv_len   NULL or device int32 [B], clamped to [0, Nk]; no block mask.
+ *   dtype    FA_BF16 only (FA_ERR_DTYPE otherwise).
+ *   num_splits  0 = chosen from the sizes (as many ranges as keep every
+ *            wave or work-group resident at once), else 1..1024; ranges are
+ *            whole tiles or cells, so fewer may be used
+ *            (fa_fwd_splitkv_num_splits reports the count).
+ *   workspace  at least fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d,
+ *            num_splits) bytes, 16-byte aligned, no initialisation needed
+ *            (nsplit x B*H*Nq x (d + 2) float32); calls sharing a workspace
+ *            must not overlap in time.
+ * Errors as fa_fwd; FA_ERR_ARG also for num_splits outside 0..1024.  Nk = 0
+ * gives O = 0 and lse = -inf.  k and v may be NULL when Nk = 0.
+ */
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
+
+/* Number of key ranges fa_fwd_splitkv uses for these sizes (0 for empty or
+ * invalid sizes). */
+int fa_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int num_splits);
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                   const int32_t* kv_len, int dtype, int num_splits,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated name of a status code. */
 const char* fa_status_str(int status);
 

@@ -140,6 +140,41 @@ def test_dropout_validation(lib):
     assert r == 7
 
 
+def test_splitkv_plan_and_validation(lib):
+    # At most 4 queries: one wave per (range, b, h), ranges of whole 64-key
+    # tiles, when chosen as many as give one wave per SIMD (1024 = 256
+    # compute units x 4).  More queries: one work-group per (range, b, h, 128
+    # queries), ranges of whole 128-key cells, 512 resident work-groups.
+    assert lib.fa_fwd_splitkv_num_splits(1, 1, 1, 16384, 0) == 256       # one tile each
+    assert lib.fa_fwd_splitkv_num_splits(16, 16, 1, 16384, 0) == 4
+    assert lib.fa_fwd_splitkv_num_splits(4, 16, 4, 16384, 0) == 16
+    assert lib.fa_fwd_splitkv_num_splits(3, 16, 1, 16384, 0) == 20       # 21 asked, 13 tiles each
+    assert lib.fa_fwd_splitkv_num_splits(1, 1, 1, 1000, 3) == 3
+    assert lib.fa_fwd_splitkv_num_splits(1, 1, 1, 300, 64) == 5          # clamped to the tiles
+    assert lib.fa_fwd_splitkv_num_splits(1, 1, 5, 300, 64) == 3          # clamped to the cells
+    assert lib.fa_fwd_splitkv_num_splits(1, 16, 2048, 16384, 0) == 2
+    assert lib.fa_fwd_splitkv_num_splits(3, 16, 5, 16384, 0) == 10       # 480 work-groups, not 528
+    assert lib.fa_fwd_splitkv_num_splits(8, 16, 4096, 16384, 0) == 1     # 4096 groups already
+    assert lib.fa_fwd_splitkv_num_splits(1, 1, 1, 0, 0) == 1
+    assert lib.fa_fwd_splitkv_num_splits(1, 1, 1, 100, 1025) == 0
+    assert lib.fa_fwd_splitkv_workspace_bytes(2, 3, 5, 1000, 64, 3) == 3 * 2 * 3 * 5 * (64 + 2) * 4
+    assert lib.fa_fwd_splitkv_workspace_bytes(2, 3, 0, 1000, 64, 3) == 0
+    P = FAKE
+    need = lib.fa_fwd_splitkv_workspace_bytes(1, 2, 10, 500, 128, 0)
+
+    def call(ws=P, nbytes=need, dtype=0, ns=0, d=128, scale=0.1, Nk=500, k=P):
+        return lib.fa_fwd_splitkv(P, k, P, P, P, 1, 2, 10, Nk, d, scale, 1, None, dtype, ns, ws, nbytes, None)
+    assert call(dtype=1) == 3                         # bf16 only
+    assert call(d=96) == 2
+    assert call(ns=1025) == 7 and call(ns=-1) == 7
+    assert call(scale=0.0) == 7
+    assert call(ws=None) == 1
+    assert call(ws=P + 8) == 4
+    assert call(nbytes=need - 1) == 5
+    assert call(k=None) == 1
+    assert lib.fa_fwd_splitkv(P, P, P, P, P, 1, 2, 0, 500, 128, 0.1, 0, None, 0, 0, None, 0, None) == 0
+
+
 def test_debug_visits_validation(lib):
     assert lib.fa_debug_visits(3, 1, 1, 128, 64, 0, None, None, 0, FAKE, None, 0, None) == 7
     assert lib.fa_debug_visits(0, 1, 1, 128, 64, 0, None, None, 0, None, None, 0, None) == 1

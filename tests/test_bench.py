@@ -57,3 +57,19 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_splitkv_pairs_and_bounds():
+    """Allowed pairs under the bottom-right causal mask, against a brute-force
+    count; decode is bandwidth-bound and chunked prefill matrix-bound."""
+    from workloads import SPLITKV_WORKLOADS
+    for Nq, Nk in ((1, 7), (3, 3), (5, 12), (9, 4)):
+        i, j = np.arange(Nq)[:, None], np.arange(Nk)[None, :]
+        assert bench.splitkv_pairs(Nq, Nk, True) == int((j <= i + Nk - Nq).sum())
+        assert bench.splitkv_pairs(Nq, Nk, False) == Nq * Nk
+    ridge = bench.PEAK_BF16_TFLOPS * 1e12 / (bench.PEAK_HBM_GBS * 1e9)
+    f, b = bench.splitkv_alg(SPLITKV_WORKLOADS["decode"])
+    assert f / b < ridge
+    assert b == 2 * 256 * (2 + 2 * 16384) * 128 + 4 * 256
+    f, b = bench.splitkv_alg(SPLITKV_WORKLOADS["prefill"])
+    assert f / b > ridge

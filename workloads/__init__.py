@@ -93,6 +93,50 @@ def draw_qkvdo(B, H, N, d, dtype="bf16", sigma=1.0, seed=0):
     return tuple(out)
 
 
+# Split-key forward workloads: few queries against a long key/value sequence
+# (the small-batch, long-prompt inference case of the sequence-parallel
+# discussion).  Values as the long-context workload: N(0, 0.5), bf16.
+SPLITKV_WORKLOADS = {
+    "decode": dict(B=16, H=16, Nq=1, Nk=16384, d=128, causal=False, sigma=math.sqrt(0.5), seed=21,
+                   desc="decode: B=16 H=16, one query against 16384 keys, d=128 bf16, scale 1/sqrt(128)"),
+    "prefill": dict(B=1, H=16, Nq=2048, Nk=16384, d=128, causal=True, sigma=math.sqrt(0.5), seed=22,
+                    desc="chunked prefill: the last 2048 queries of the 16384-token causal long context, "
+                         "B=1 H=16 d=128 bf16, scale 1/sqrt(128)"),
+}
+
+
+def draw_split_qkv(B, H, Nq, Nk, d, sigma=1.0, seed=0):
+    """Q [B,H,Nq,d], K and V [B,H,Nk,d] as bf16-exact fp32 arrays.  Batch entry
+    b of tensor t (0 = Q, 1 = K, 2 = V) is fp32 standard normals drawn from
+    PCG64(seed) jumped 3 b + t + 1 times, times sigma, rounded to bf16
+    (nearest, ties to even).  Entries are drawn on parallel threads."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    base = np.random.PCG64(seed)
+    out = [np.empty((B, H, n, d), np.float32) for n in (Nq, Nk, Nk)]
+
+    def fill(job):
+        b, t = job
+        rng = np.random.Generator(base.jumped(3 * b + t + 1))
+        x = rng.standard_normal(out[t].shape[1:], dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        out[t][b] = _bf16_round_finite(x)
+
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(fill, [(b, t) for b in range(B) for t in range(3)]))
+    return tuple(out)
+
+
+def _bf16_round_finite(x: np.ndarray) -> np.ndarray:
+    """bf16_round's values for finite fp32 input, in 32-bit integer arithmetic
+    (no carry leaves 32 bits for finite values)."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16
+    return (r << 16).view(np.float32)
+
+
 def draw_kv_len(B, lo, hi, seed):
     rng = np.random.Generator(np.random.PCG64(seed))
     return rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
