@@ -325,3 +325,25 @@ def test_key_splits_merge_to_the_full_softmax():
         m_run, l_run = m_new, l_new
     assert np.allclose(acc / l_run[:, None], O, rtol=1e-12, atol=1e-12)
     assert np.allclose(m_run + np.log(l_run), lse, rtol=1e-12, atol=1e-12)
+
+
+def test_offset_causal_is_the_tail_of_the_square_problem():
+    """The last Nq rows of the square causal problem over Nk positions are the
+    offset problem with those Nq queries; with more queries than keys the first
+    Nq - Nk rows have no key (O = 0, lse = -inf) and the rest see j <= i - (Nq - Nk)."""
+    rng = np.random.Generator(np.random.PCG64(62))
+    Nk, d, scale = 40, 5, 0.6
+    Q, K, V = rng.standard_normal((Nk, d)), rng.standard_normal((Nk, d)), rng.standard_normal((Nk, d))
+    O_sq, lse_sq = attention.head_forward(Q, K, V, scale, causal=True)
+    for Nq in (1, 7, 40):
+        O, lse = attention.head_forward(Q[Nk - Nq:], K, V, scale, causal=True, causal_offset=Nk - Nq)
+        assert np.allclose(O, O_sq[Nk - Nq:], rtol=1e-13, atol=1e-13)
+        assert np.allclose(lse, lse_sq[Nk - Nq:], rtol=1e-13, atol=1e-13)
+    Nq = 46
+    Qx = rng.standard_normal((Nq, d))
+    O, lse = attention.head_forward(Qx, K, V, scale, causal=True, causal_offset=Nk - Nq)
+    assert np.all(O[:Nq - Nk] == 0) and np.all(np.isneginf(lse[:Nq - Nk]))
+    # row Nq - Nk + t sees keys 0..t, exactly like square row t
+    Osq2, lsesq2 = attention.head_forward(Qx[Nq - Nk:], K, V, scale, causal=True)
+    assert np.allclose(O[Nq - Nk:], Osq2, rtol=1e-13, atol=1e-13)
+    assert np.allclose(lse[Nq - Nk:], lsesq2, rtol=1e-13, atol=1e-13)
