@@ -16,7 +16,8 @@ cpu_baseline times the fp64 CPU oracle (forward + backward) on two heads of
 the same workload.
 
 --workload K times one of the other workloads (1 tiny fp32, 2 GPT-2 shaped,
-3 BERT-shaped with key padding, 5 block-sparse 64K) with the same step and
+3 BERT-shaped with key padding, 5 block-sparse 64K, 6 long context at head
+dimension 256) with the same step and
 prints the same kind of line (no CPU leg unless --cpu-baseline is given); the
 default line is the long-context workload.  Per kernel it reports achieved
 TFLOP/s against the bf16 matrix peak and achieved GB/s of compulsory HBM
@@ -413,7 +414,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=4, choices=(1, 2, 3, 4, 5),
+    ap.add_argument("--workload", type=int, default=4, choices=(1, 2, 3, 4, 5, 6),
                     help="workload to time (default 4, the long-context line)")
     ap.add_argument("--sweep", action="store_true", help="time the N = 1K..16K sweep (one JSON line per shape)")
     ap.add_argument("--dropout", type=float, default=0.0,
@@ -483,6 +484,7 @@ def main():
             2: "GPT-2 shaped: B=8 H=12 N=1024 d=64 bf16 causal, scale 1/8",
             3: "BERT-large shaped: B=32 H=16 N=512 d=64 bf16, key padding kv_len ~ U[128, 512], scale 1/8",
             4: "long-context: B=1 H=16 N=16384 d=128 bf16 causal, scale 1/sqrt(128)",
+            6: "long-context, head dim 256: B=1 H=8 N=16384 d=256 bf16 causal, scale 1/16",
             5: "block-sparse: B=1 H=8 N=65536 d=64 bf16, 128x128 cell mask (band, 2 random cells per row, "
                "first column), scale 1/8"}[args.workload]
     config = {"workload": desc, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,

@@ -25,7 +25,7 @@ struct Shape {
 int check_shape(const Shape& s, const uint8_t* block_mask, bool* empty) {
   if (s.dtype != FA_BF16 && s.dtype != FA_F32) return FA_ERR_DTYPE;
   if (s.B < 0 || s.H < 0 || s.N < 0) return FA_ERR_SHAPE;
-  if (s.d != 64 && s.d != 128) return FA_ERR_SHAPE;
+  if (s.d != 64 && s.d != 128 && !(s.d == 256 && s.dtype == FA_BF16)) return FA_ERR_SHAPE;
   *empty = (s.B == 0 || s.H == 0 || s.N == 0);
   if (*empty) return FA_OK;
   const long long T = (s.N + kCell - 1) / kCell;
@@ -213,7 +213,7 @@ int pre_impl(const void* o, const void* dO, float* delta, int B, int H, int N, i
 }
 
 size_t split_bytes(int N, int d, int dtype, int has_block_mask) {
-  if (N <= 0 || (d != 64 && d != 128) || dtype != FA_BF16 || !has_block_mask) return 0;
+  if (N <= 0 || (d != 64 && d != 128 && d != 256) || dtype != FA_BF16 || !has_block_mask) return 0;
   return fa::split_ws_bytes(N, d);
 }
 
@@ -283,7 +283,7 @@ int splitkv_plan(int B, int H, int Nq, int Nk, int num_splits, KvPlan* p) {
 int check_splitkv_shape(int B, int H, int Nq, int Nk, int d, int dtype, bool* empty) {
   if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_DTYPE;
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_SHAPE;
   *empty = (B == 0 || H == 0 || Nq == 0);
   if (*empty) return FA_OK;
   if (dtype != FA_BF16) return FA_ERR_DTYPE;

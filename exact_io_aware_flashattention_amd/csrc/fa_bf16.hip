@@ -64,6 +64,9 @@ struct FwdB {
   static constexpr int TILE = BC * D * 2;       // bytes of one K or V tile
   static constexpr int SSTEPS = D / 16;
   static constexpr int NB = D / 32;
+  // waves per SIMD: two (<= 256 registers) up to d = 128; d = 256 needs the
+  // accumulation registers of a single wave per SIMD
+  static constexpr int OCC = D == 256 ? 1 : 2;
 };
 
 // Forward, software-pipelined over 32-key sub-blocks t = 0, 1, ... of the walk:
@@ -76,7 +79,8 @@ struct FwdB {
 // one barrier and one DMA issue (K of tile j+2, V of tile j+1), so every tile
 // is requested two sub-block steps before it is read.
 template <int D, int MODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC, FwdB<D>::OCC))) void fwd_bf16_kernel(
+    AttnArgs a) {
   using C = FwdB<D>;
   constexpr bool WALK_ONLY = MODE == K_WALK, DROP = MODE == K_DROP, SPLITKV = MODE == K_SPLITKV;
   __shared__ u32x4 drop_xch[DROP ? NT : 1];
@@ -326,25 +330,34 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
 template <int D>
 struct DkdvB {
-  static constexpr int BQ = D == 128 ? 32 : 64;     // queries per stage
-  static constexpr int TSH = D == 128 ? 5 : 6;
+  static constexpr int BQ = D >= 128 ? 32 : 64;     // queries per stage
+  static constexpr int TSH = D >= 128 ? 5 : 6;
   static constexpr int QS = BQ / 32;
   static constexpr int TILE = BQ * D * 2;           // one Q or dO tile (bytes)
   static constexpr int STAGE = 2 * TILE + 2 * BQ * 4;   // Q, dO, lse*log2e, delta
   static constexpr int VRES = CELL * D * 2;         // V of the work-group's 128 keys
   static constexpr int SSTEPS = D / 16;
   static constexpr int NB = D / 32;
+  // waves per SIMD
+  static constexpr int occ(int pass) { return D == 256 ? 1 : 2; }
 };
 
 // SPLIT (block mask present): work-groups [0, SPLIT_MAX_ITEMS) take the split
 // items of the plan (a chunk of a long column each; surplus ones exit), the
 // rest take one column each and exit if the column is split.
-template <int D, int MODE, bool SPLIT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_bf16_kernel(AttnArgs a) {
+// PASS: 0 accumulates dK and dV together; 1 only dV (S, P); 2 only dK (S, dP,
+// dS).  d = 256 runs passes 1 and 2: dK and dV together would need 256
+// accumulator registers per lane besides K's 64, more than one wave holds
+// without spilling; each pass holds half, for one more Q K^T product.
+template <int D, int MODE, bool SPLIT, int PASS = 0>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DkdvB<D>::occ(PASS), DkdvB<D>::occ(PASS)))) void
+dkdv_bf16_kernel(AttnArgs a) {
   using C = DkdvB<D>;
   constexpr bool WALK_ONLY = MODE == K_WALK, DROP = MODE == K_DROP;
+  constexpr bool DO_DV = PASS != 2, DO_DK = PASS != 1;
   __shared__ u32x4 drop_xch[DROP ? NT : 1];
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[WALK_ONLY ? 16 : C::VRES + 2 * C::STAGE];
+  constexpr int VRES = C::VRES;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[WALK_ONLY ? 16 : VRES + 2 * C::STAGE];
   __shared__ int cell_list[MAX_T];
   __shared__ int scratch4[4];
 
@@ -404,16 +417,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
     for (int s = 0; s < C::SSTEPS; ++s)
       kf[s] = myk < N ? ld16(Kg + (size_t)myk * D + s * 16 + 8 * h) : u32x4{0, 0, 0, 0};
-    f32x16 dk[C::NB], dv[C::NB];
+    f32x16 dk[DO_DK ? C::NB : 1], dv[DO_DV ? C::NB : 1];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
-      zero(dk[nb]);
-      zero(dv[nb]);
+      if constexpr (DO_DK) zero(dk[nb]);
+      if constexpr (DO_DV) zero(dv[nb]);
     }
 
     float st_l = 0.f, st_d = 0.f;   // this thread's row statistics of the next tile
     auto issue = [&](int it) {
-      unsigned char* st = smem + C::VRES + (it & 1) * C::STAGE;
+      unsigned char* st = smem + VRES + (it & 1) * C::STAGE;
       const int q0 = walk.tile_start(it);
       dma.load(Qh, N, q0, st);
       dma.load(dOh, N, q0, st + C::TILE);
@@ -425,13 +438,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
     };
     if (walk.ntiles > 0) {
-      TileDma<D, CELL>().load(reinterpret_cast<const bf16*>(a.v) + head, N, kj * CELL, Vs);
+      if constexpr (DO_DK) TileDma<D, CELL>().load(reinterpret_cast<const bf16*>(a.v) + head, N, kj * CELL, Vs);
       issue(0);
     }
 
     for (int it = 0; it < walk.ntiles; ++it) {
       wait_loads();
-      unsigned char* st = smem + C::VRES + (it & 1) * C::STAGE;
+      unsigned char* st = smem + VRES + (it & 1) * C::STAGE;
       float* stats = reinterpret_cast<float*>(st + 2 * C::TILE);
       if (tid < C::BQ) {
         stats[tid] = st_l;
@@ -453,8 +466,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
         for (int k = 0; k < C::SSTEPS; ++k) {
           mma(s, as_bf16x8(row_chunk<D>(Qs, 32 * qs + l32, 2 * k + h)), as_bf16x8(kf[k]));
-          mma(dp, as_bf16x8(row_chunk<D>(dOs, 32 * qs + l32, 2 * k + h)),
-              as_bf16x8(row_chunk<D>(Vs, wave * 32 + l32, 2 * k + h)));
+          if constexpr (DO_DK)
+            mma(dp, as_bf16x8(row_chunk<D>(dOs, 32 * qs + l32, 2 * k + h)),
+                as_bf16x8(row_chunk<D>(Vs, wave * 32 + l32, 2 * k + h)));
         }
         // P = exp2(s c - lse log2 e), dS = P (dP - delta); register r <-> query
         // q0 + 32 qs + acc_row(r, h).  On edge tiles an entry is masked iff the
@@ -482,9 +496,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
               // dV uses P Z (the 1 / (1 - p) factor is applied at the end);
               // dS = P ((dO V^T) Z - delta)
               const bool keep = keep_byte(keepw[g], e, a.drop_t);
-              dp[r] = s[r] * ((keep ? dp[r] * a.drop_inv : 0.f) - d4[e]);
+              if constexpr (DO_DK) dp[r] = s[r] * ((keep ? dp[r] * a.drop_inv : 0.f) - d4[e]);
               if (!keep) s[r] = 0.f;
-            } else {
+            } else if constexpr (DO_DK) {
               dp[r] = s[r] * (dp[r] - d4[e]);
             }
           }
@@ -496,14 +510,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             if (acc_row(r, 0) < lim) s[r] = dp[r] = 0.f;
         }
         // dV^T += dO^T P and dK^T += Q^T dS, the transposed operands read from the row-major tiles
-        const PackedB pb = pack_bf16(s), db = pack_bf16(dp);
+        if constexpr (PASS == 0) {
+          const PackedB pb = pack_bf16(s), db = pack_bf16(dp);
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
+          for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
-            mma(dv[nb], tr_operand<D>(dOs, 32 * qs + 16 * mm, 32 * nb), pb.p[mm]);
-            mma(dk[nb], tr_operand<D>(Qs, 32 * qs + 16 * mm, 32 * nb), db.p[mm]);
-          }
+            for (int mm = 0; mm < 2; ++mm) {
+              mma(dv[nb], tr_operand<D>(dOs, 32 * qs + 16 * mm, 32 * nb), pb.p[mm]);
+              mma(dk[nb], tr_operand<D>(Qs, 32 * qs + 16 * mm, 32 * nb), db.p[mm]);
+            }
+        } else if constexpr (DO_DV) {
+          const PackedB pb = pack_bf16(s);
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) mma(dv[nb], tr_operand<D>(dOs, 32 * qs + 16 * mm, 32 * nb), pb.p[mm]);
+        } else {
+          const PackedB db = pack_bf16(dp);
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) mma(dk[nb], tr_operand<D>(Qs, 32 * qs + 16 * mm, 32 * nb), db.p[mm]);
+        }
       }
     }
 
@@ -522,10 +550,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const size_t o = ((size_t)(8 * nb + 2 * g + h) * CELL + kl) * 4;
-            *reinterpret_cast<f32x4*>(slot + o) =
-                f32x4{dk[nb][4 * g], dk[nb][4 * g + 1], dk[nb][4 * g + 2], dk[nb][4 * g + 3]};
-            *reinterpret_cast<f32x4*>(slot + CELL * D + o) =
-                f32x4{dv[nb][4 * g], dv[nb][4 * g + 1], dv[nb][4 * g + 2], dv[nb][4 * g + 3]};
+            if constexpr (DO_DK)
+              *reinterpret_cast<f32x4*>(slot + o) =
+                  f32x4{dk[nb][4 * g], dk[nb][4 * g + 1], dk[nb][4 * g + 2], dk[nb][4 * g + 3]};
+            if constexpr (DO_DV)
+              *reinterpret_cast<f32x4*>(slot + CELL * D + o) =
+                  f32x4{dv[nb][4 * g], dv[nb][4 * g + 1], dv[nb][4 * g + 2], dv[nb][4 * g + 3]};
           }
         __threadfence();   // release this thread's partials at device scope
         __syncthreads();
@@ -536,8 +566,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         // the last chunk adds all partials of the column in chunk order
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
-          zero(dk[nb]);
-          zero(dv[nb]);
+          if constexpr (DO_DK) zero(dk[nb]);
+          if constexpr (DO_DV) zero(dv[nb]);
         }
         for (int c = 0; c < nchunk; ++c) {
           const float* sl = a.split.slots + (size_t)(first + c) * (2 * CELL * D);
@@ -546,12 +576,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const size_t o = ((size_t)(8 * nb + 2 * g + h) * CELL + kl) * 4;
-              const f32x4 x = *reinterpret_cast<const f32x4*>(sl + o);
-              const f32x4 y = *reinterpret_cast<const f32x4*>(sl + CELL * D + o);
+              if constexpr (DO_DK) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(sl + o);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                dk[nb][4 * g + e] += x[e];
-                dv[nb][4 * g + e] += y[e];
+                for (int e = 0; e < 4; ++e) dk[nb][4 * g + e] += x[e];
+              }
+              if constexpr (DO_DV) {
+                const f32x4 y = *reinterpret_cast<const f32x4*>(sl + CELL * D + o);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dv[nb][4 * g + e] += y[e];
               }
             }
         }
@@ -565,10 +598,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int c = 32 * nb + 8 * g + 4 * h;
-          store4(dkp + c, dk[nb][4 * g] * a.scale, dk[nb][4 * g + 1] * a.scale, dk[nb][4 * g + 2] * a.scale,
-                 dk[nb][4 * g + 3] * a.scale);
+          if constexpr (DO_DK)
+            store4(dkp + c, dk[nb][4 * g] * a.scale, dk[nb][4 * g + 1] * a.scale, dk[nb][4 * g + 2] * a.scale,
+                   dk[nb][4 * g + 3] * a.scale);
           const float vs = DROP ? a.drop_inv : 1.f;
-          store4(dvp + c, dv[nb][4 * g] * vs, dv[nb][4 * g + 1] * vs, dv[nb][4 * g + 2] * vs, dv[nb][4 * g + 3] * vs);
+          if constexpr (DO_DV)
+            store4(dvp + c, dv[nb][4 * g] * vs, dv[nb][4 * g + 1] * vs, dv[nb][4 * g + 2] * vs,
+                   dv[nb][4 * g + 3] * vs);
         }
     }
   }
@@ -583,10 +619,12 @@ struct DqB {
   static constexpr int STAGE = 2 * TILE;        // K, V
   static constexpr int SSTEPS = D / 16;
   static constexpr int NB = D / 32;
+  static constexpr int OCC = D == 256 ? 1 : 2;  // waves per SIMD
 };
 
 template <int D, int MODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DqB<D>::OCC, DqB<D>::OCC))) void dq_bf16_kernel(
+    AttnArgs a) {
   using C = DqB<D>;
   constexpr bool WALK_ONLY = MODE == K_WALK, DROP = MODE == K_DROP;
   __shared__ u32x4 drop_xch[DROP ? NT : 1];
@@ -737,28 +775,51 @@ FA_DEFINE_LAUNCH(launch_dq_b, dq_bf16_kernel)
 
 // dK/dV: with a block mask the split plan runs first and SPLIT_MAX_ITEMS
 // work-groups for split items precede the per-column ones.
-template <int D>
-static hipError_t launch_dkdv_b(const AttnArgs& a, bool walk_only, hipStream_t s) {
+template <int D, int PASS>
+static hipError_t launch_dkdv_pass(const AttnArgs& a, bool walk_only, hipStream_t s) {
   const long long ncol = (long long)((a.N + CELL - 1) / CELL) * a.H * a.B;
-  if (!a.mask) {
-    if (walk_only)
-      hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_WALK, false>), dim3((unsigned)ncol), dim3(NT), 0, s, a);
-    else if (a.drop_t)
-      hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_DROP, false>), dim3((unsigned)ncol), dim3(NT), 0, s, a);
+  const long long nwg = a.mask ? SPLIT_MAX_ITEMS + ncol : ncol;
+  if (a.mask) {
+    // (the plan also clears the arrival counters, so every pass gets its own)
+    const hipError_t e = launch_split_plan(a, s);
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)nwg), block(NT);
+  if (walk_only) {
+    if (a.mask)
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_WALK, true>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_PLAIN, false>), dim3((unsigned)ncol), dim3(NT), 0, s, a);
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_WALK, false>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  const hipError_t e = launch_split_plan(a, s);
-  if (e != hipSuccess) return e;
-  const long long nwg = SPLIT_MAX_ITEMS + ncol;
-  if (walk_only)
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_WALK, true>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
-  else if (a.drop_t)
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_DROP, true>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
-  else
-    hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_PLAIN, true>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
-  return hipGetLastError();
+  if constexpr (D == 256 && PASS == 0) {
+    return hipErrorInvalidValue;   // d = 256 computes in passes 1 and 2 only
+  } else {
+    if (a.mask) {
+      if (a.drop_t)
+        hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_DROP, true, PASS>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_PLAIN, true, PASS>), grid, block, 0, s, a);
+    } else {
+      if (a.drop_t)
+        hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_DROP, false, PASS>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_PLAIN, false, PASS>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+  }
+}
+
+template <int D>
+static hipError_t launch_dkdv_b(const AttnArgs& a, bool walk_only, hipStream_t s) {
+  if constexpr (D == 256) {
+    if (walk_only) return launch_dkdv_pass<D, 0>(a, true, s);
+    const hipError_t e = launch_dkdv_pass<D, 1>(a, false, s);
+    if (e != hipSuccess) return e;
+    return launch_dkdv_pass<D, 2>(a, false, s);
+  } else {
+    return launch_dkdv_pass<D, 0>(a, walk_only, s);
+  }
 }
 
 // Merge of the key ranges of a split-key forward (one thread per row and four
@@ -798,6 +859,8 @@ hipError_t launch_splitkv_merge(const AttnArgs& a, int d, hipStream_t s) {
   const dim3 grid((unsigned)((threads + NT - 1) / NT));
   if (d == 64)
     hipLaunchKernelGGL((splitkv_merge_kernel<64>), grid, dim3(NT), 0, s, a);
+  else if (d == 256)
+    hipLaunchKernelGGL((splitkv_merge_kernel<256>), grid, dim3(NT), 0, s, a);
   else
     hipLaunchKernelGGL((splitkv_merge_kernel<128>), grid, dim3(NT), 0, s, a);
   return hipGetLastError();
@@ -815,17 +878,23 @@ static hipError_t launch_splitkv_b(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fwd_splitkv_bf16(const AttnArgs& a, int d, hipStream_t s) {
-  return d == 64 ? launch_splitkv_b<64>(a, s) : launch_splitkv_b<128>(a, s);
+  return d == 64 ? launch_splitkv_b<64>(a, s) : d == 256 ? launch_splitkv_b<256>(a, s) : launch_splitkv_b<128>(a, s);
 }
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s) {
-  return d == 64 ? launch_fwd_b<64>(a, walk_only, s) : launch_fwd_b<128>(a, walk_only, s);
+  return d == 64    ? launch_fwd_b<64>(a, walk_only, s)
+         : d == 256 ? launch_fwd_b<256>(a, walk_only, s)
+                    : launch_fwd_b<128>(a, walk_only, s);
 }
 hipError_t launch_dkdv_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s) {
-  return d == 64 ? launch_dkdv_b<64>(a, walk_only, s) : launch_dkdv_b<128>(a, walk_only, s);
+  return d == 64    ? launch_dkdv_b<64>(a, walk_only, s)
+         : d == 256 ? launch_dkdv_b<256>(a, walk_only, s)
+                    : launch_dkdv_b<128>(a, walk_only, s);
 }
 hipError_t launch_dq_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s) {
-  return d == 64 ? launch_dq_b<64>(a, walk_only, s) : launch_dq_b<128>(a, walk_only, s);
+  return d == 64    ? launch_dq_b<64>(a, walk_only, s)
+         : d == 256 ? launch_dq_b<256>(a, walk_only, s)
+                    : launch_dq_b<128>(a, walk_only, s);
 }
 
 }  // namespace fa

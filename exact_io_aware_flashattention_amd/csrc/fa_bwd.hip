@@ -501,7 +501,8 @@ static hipError_t launch_dq_t(const AttnArgs& a, bool walk_only, hipStream_t s) 
 }
 
 hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int d, hipStream_t s) {
-  if (dtype == 0) return d == 64 ? launch_pre_t<bf16, 64>(a, s) : launch_pre_t<bf16, 128>(a, s);
+  if (dtype == 0)
+    return d == 64 ? launch_pre_t<bf16, 64>(a, s) : d == 256 ? launch_pre_t<bf16, 256>(a, s) : launch_pre_t<bf16, 128>(a, s);
   return d == 64 ? launch_pre_t<float, 64>(a, s) : launch_pre_t<float, 128>(a, s);
 }
 

@@ -42,7 +42,7 @@ struct DecCfg {
   static constexpr int LPR = D / 8;      // lanes per key row (16 bytes each)
   static constexpr int KPI = 64 / LPR;   // key rows per load instruction
   static constexpr int G = 8;            // load instructions per block and tensor
-  static constexpr int KB = G * KPI;     // keys per block: 32 (d = 128), 64 (d = 64)
+  static constexpr int KB = G * KPI;     // keys per block: 16 (d = 256), 32 (d = 128), 64 (d = 64)
 };
 
 // Cache policy of the K and V loads: non-temporal (each byte is read once).
@@ -63,6 +63,7 @@ __device__ __forceinline__ float row_sum(float x) {
   x += xch(x, std::integral_constant<int, 0x4E>());    // quad_perm [2,3,0,1]: lane ^ 2
   if constexpr (LPR >= 8) x += xch(x, std::integral_constant<int, 0x141>());    // row_half_mirror: 7 - lane
   if constexpr (LPR >= 16) x += xch(x, std::integral_constant<int, 0x140>());   // row_mirror: 15 - lane
+  if constexpr (LPR >= 32) x += __shfl_xor(x, 16);                                  // the other row of 16
   return x;
 }
 
@@ -255,7 +256,7 @@ hipError_t launch_decode_d(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_decode_bf16(const AttnArgs& a, int d, hipStream_t s) {
-  return d == 64 ? launch_decode_d<64>(a, s) : launch_decode_d<128>(a, s);
+  return d == 64 ? launch_decode_d<64>(a, s) : d == 256 ? launch_decode_d<256>(a, s) : launch_decode_d<128>(a, s);
 }
 
 }  // namespace fa

@@ -13,7 +13,10 @@
 //     4 consecutive rows (4k .. 4k+3) x 4 consecutive chunks.
 // d = 128: swz(r) = 4 (r % 4) + (r / 4) % 4;  d = 64: swz(r) = 4 ((r / 2) % 2)
 // + (r / 4) % 4.  Both satisfy both conditions (checked with the LDS bank
-// conflict counter: 4 cycles per row read, 2 per transposed read).
+// conflict counter: 4 cycles per row read, 2 per transposed read).  A 512-byte
+// row (d = 256) spans two bank lines; the bank of chunk p is p % 16, and the
+// XOR with swz(r) < 16 changes only those four bits, so the d = 128 swizzle
+// serves d = 256 unchanged.
 //
 // Loads: buffer_load_dwordx4 with the LDS-destination form writes 64 lanes x
 // 16 bytes contiguously at the LDS address in M0, so lane t of a load
@@ -41,7 +44,7 @@ struct BTile {
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
   static constexpr int ROWS_PER_LOAD = 1024 / ROWB;   // rows one wave-wide load fills
   __host__ __device__ static constexpr int swz(int r) {
-    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    return D >= 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
   }
   __device__ static __forceinline__ int off(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
 };
@@ -70,12 +73,15 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, unsigned char* lds, int voff) 
 
 // Loads of an R-row tile spread over the NW waves of the work-group: wave w
 // issues the wave-wide loads i = j * NW + w (j < NJ), load i filling rows
-// [i * RPL, (i + 1) * RPL) (RPL rows per 1024 bytes).  The swizzle repeats
-// every NW * RPL rows (checked below), so the logical chunk a lane fetches is
-// the same for every j and the lane's byte offset inside the tile is
-// voff[0] + j * NW * 1024: the per-lane offsets are computed once per kernel,
-// and a tile load costs only scalar work (a buffer resource based at the
-// tile's first row) plus the load instructions.
+// [i * RPL, (i + 1) * RPL) (RPL rows per 1024 bytes).  When the swizzle
+// repeats every NW * RPL rows (d = 64, 128) the logical chunk a lane fetches
+// is the same for every j and the lane's byte offset inside the tile is
+// voff[0] + j * NW * 1024; otherwise (d = 256, two rows per load) the offsets
+// of one swizzle period are kept and each later period gets its own buffer
+// resource based at its first row (the range check of a buffer load covers the
+// per-lane offset, so rows past N still read as zeros).  Either way the
+// per-lane offsets are computed once per kernel, and a tile load costs only
+// scalar work plus the load instructions.
 template <int D, int NW>
 __host__ __device__ constexpr bool swizzle_repeats(int nj) {
   for (int w = 0; w < NW; ++w)
@@ -86,31 +92,65 @@ __host__ __device__ constexpr bool swizzle_repeats(int nj) {
   return true;
 }
 
+// Smallest k such that the swizzle repeats every k * NW loads (1 for d = 64
+// and 128; 2 for d = 256, whose 16-row swizzle period spans 8 two-row loads).
+template <int D, int NW>
+__host__ __device__ constexpr int swizzle_period_loads() {
+  for (int k = 1; k < 16; ++k) {
+    bool ok = true;
+    for (int r = 0; r < 64; ++r)
+      if (BTile<D>::swz(r + k * NW * BTile<D>::ROWS_PER_LOAD) != BTile<D>::swz(r)) ok = false;
+    if (ok) return k;
+  }
+  return 16;
+}
+
 template <int D, int R, int NW = NT / 64>
 struct TileDma {
   using TL = BTile<D>;
   static constexpr int NLOAD = R / TL::ROWS_PER_LOAD;
   static constexpr int NJ = NLOAD / NW;
+  static constexpr int KP = swizzle_period_loads<D, NW>();
   static_assert(NLOAD % NW == 0, "wave-wide loads must divide evenly over the waves");
-  static_assert(swizzle_repeats<D, NW>(NJ), "swizzle must repeat every NW loads");
-  int voff[NJ];
+  static_assert(KP == 1 ? swizzle_repeats<D, NW>(NJ) : NJ % KP == 0, "loads must cover whole swizzle periods");
+  // KP == 1: one offset per load; KP > 1: the KP offsets of one period,
+  // relative to the period's first row.
+  int voff[KP == 1 ? NJ : KP];
 
   __device__ __forceinline__ TileDma() {
     const int lane = threadIdx.x & 63, wave = wave_id();
-    const int lr = wave * TL::ROWS_PER_LOAD + lane / TL::CPR;   // row of load j = 0
-    const int c = (lane % TL::CPR) ^ TL::swz(lr);               // logical chunk at position lane
-    const int off0 = (lr * D + c * 8) * 2;
+    if constexpr (KP == 1) {
+      const int lr = wave * TL::ROWS_PER_LOAD + lane / TL::CPR;   // row of load j = 0
+      const int c = (lane % TL::CPR) ^ TL::swz(lr);               // logical chunk at position lane
+      const int off0 = (lr * D + c * 8) * 2;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) voff[j] = off0 + j * NW * 1024;
+      for (int j = 0; j < NJ; ++j) voff[j] = off0 + j * NW * 1024;
+    } else {
+#pragma unroll
+      for (int j = 0; j < KP; ++j) {
+        const int lr = (j * NW + wave) * TL::ROWS_PER_LOAD + lane / TL::CPR;
+        const int c = (lane % TL::CPR) ^ TL::swz(lr);
+        voff[j] = (lr * D + c * 8) * 2;
+      }
+    }
   }
   // Issue the loads of rows [row0, row0 + R) of head (N rows) into lds
   // (R * D * 2 bytes); rows at or past N read as zeros.  Completion:
   // s_waitcnt vmcnt(0) in every wave, then a barrier.
   __device__ __forceinline__ void load(const void* head, int N, int row0, unsigned char* lds) const {
-    const u32x4 rsrc = rows_rsrc(head, N, D, row0);
     const int wave = wave_id();
+    if constexpr (KP == 1) {
+      const u32x4 rsrc = rows_rsrc(head, N, D, row0);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) dma16(rsrc, lds + (j * NW + wave) * 1024, voff[j]);
+      for (int j = 0; j < NJ; ++j) dma16(rsrc, lds + (j * NW + wave) * 1024, voff[j]);
+    } else {
+#pragma unroll
+      for (int p = 0; p < NJ / KP; ++p) {
+        const u32x4 rsrc = rows_rsrc(head, N, D, row0 + p * KP * NW * TL::ROWS_PER_LOAD);
+#pragma unroll
+        for (int jj = 0; jj < KP; ++jj) dma16(rsrc, lds + ((p * KP + jj) * NW + wave) * 1024, voff[jj]);
+      }
+    }
   }
 };
 

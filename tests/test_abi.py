@@ -77,6 +77,8 @@ def test_forward_validation(lib):
     assert fwd(lib, q=None) == 1                       # FA_ERR_NULL
     assert fwd(lib, lse=None) == 1
     assert fwd(lib, d=96) == 2                         # FA_ERR_SHAPE
+    assert fwd(lib, d=256, dtype=1) == 2               # d = 256 is bf16 only
+    assert fwd(lib, d=256, scale=-1.0) == 7            # d = 256 bf16 passes the shape check
     assert fwd(lib, N=-1) == 2
     assert fwd(lib, dtype=7) == 3                      # FA_ERR_DTYPE
     assert fwd(lib, k=FAKE + 8) == 4                   # FA_ERR_ALIGN

@@ -256,10 +256,11 @@ def test_sweep_shapes_sampled_heads(shape):
     _check_heads_dense(inp, out, _sample_heads(B, 16, 3, N + d), f"sweep N{N}d{d}")
 
 
-@pytest.mark.parametrize("key", [4, 5])
+@pytest.mark.parametrize("key", [4, 5, 6])
 def test_workload_long_sequence_sampled(key):
-    """N = 16K causal and N = 64K block-sparse: sampled rows of O, lse and dQ and
-    sampled key columns of dK, dV on two heads, against the gathered oracle."""
+    """N = 16K causal (d = 128 and 256) and N = 64K block-sparse: sampled rows of
+    O, lse and dQ and sampled key columns of dK, dV on two heads, against the
+    gathered oracle."""
     inp = make_inputs(WORKLOADS[key])
     say(f"workload {key} ({WORKLOADS[key].name}) full size")
     out = run_gpu(inp)

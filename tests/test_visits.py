@@ -45,6 +45,9 @@ CASES = [
     (1, 2, 5083, 128, True, "split", None),
     # the largest mask accepted: 2048 x 2048 cells
     (1, 1, 2048 * 128, 64, True, "band", None),
+    # head dimension 256 (dK/dV computes in two passes; the walk is shared)
+    (2, 2, 600, 256, True, "bern", "rand"),
+    (1, 2, 5083, 256, False, "split", None),
 ]
 
 
@@ -66,7 +69,7 @@ def test_walk_matches_expected(case):
     run_walks(B, H, N, d, causal, bm, kv)
 
 
-@pytest.mark.parametrize("key", [2, 3, 4, 5])
+@pytest.mark.parametrize("key", [2, 3, 4, 5, 6])
 def test_walk_workloads(key):
     w = WORKLOADS[key]
     from workloads import make_inputs

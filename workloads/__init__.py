@@ -1,14 +1,16 @@
 """Seeded synthetic workloads for the attention hot path.
 
 This module only draws random numbers and arranges them into the shapes of the
-five workloads; it holds none of the attention arithmetic.  Both the CPU oracle
+workloads; it holds none of the attention arithmetic.  Both the CPU oracle
 (through the tests and the bench) and the HIP library receive exactly the
 arrays produced here.
 
 Workload shapes follow the pages: the GPT-2 shape N=1024, d=64 (bornlex.github.io
 "Flash Attention", section "Standard Attention"), BERT-large at sequence length
 512 and the 16K / 64K block-sparse long sequences (FlashAttention reading guide,
-xyznot.com, section "Hasil").  No dataset item is used: values are i.i.d.
+xyznot.com, section "Hasil"), and head dimension 256 at the 16K shape (datacamp
+"Penjelasan Flash Attention", Flash Attention 2, "Dukungan untuk dimensi head
+yang lebih besar").  No dataset item is used: values are i.i.d.
 normals.
 
 Recipe (all randomness is numpy PCG64):
@@ -62,6 +64,9 @@ WORKLOADS = {
                 math.sqrt(0.5)),
     5: Workload(5, "block-sparse-64k", 1, 8, 65536, 64, "bf16", False, 1.0 / 8.0, 1.0,
                 block_sparse=True),
+    # head dimension 256 (the FA2 extension): the long-context shape with the
+    # same H * d and flops as workload 4
+    6: Workload(6, "long-context-d256", 1, 8, 16384, 256, "bf16", True, 1.0 / 16.0, math.sqrt(0.5)),
 }
 
 
