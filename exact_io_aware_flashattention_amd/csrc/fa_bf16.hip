@@ -338,8 +338,10 @@ struct DkdvB {
   static constexpr int VRES = CELL * D * 2;         // V of the work-group's 128 keys
   static constexpr int SSTEPS = D / 16;
   static constexpr int NB = D / 32;
-  // waves per SIMD
-  static constexpr int occ(int pass) { return D == 256 ? 1 : 2; }
+  // waves per SIMD: d = 256 holds one wave per SIMD, except the dV pass,
+  // which keeps no V tile in LDS (two work-groups fit) and needs only the dV
+  // accumulators
+  static constexpr int occ(int pass) { return D == 256 && pass != 1 ? 1 : 2; }
 };
 
 // SPLIT (block mask present): work-groups [0, SPLIT_MAX_ITEMS) take the split
@@ -356,7 +358,7 @@ dkdv_bf16_kernel(AttnArgs a) {
   constexpr bool WALK_ONLY = MODE == K_WALK, DROP = MODE == K_DROP;
   constexpr bool DO_DV = PASS != 2, DO_DK = PASS != 1;
   __shared__ u32x4 drop_xch[DROP ? NT : 1];
-  constexpr int VRES = C::VRES;
+  constexpr int VRES = DO_DK ? C::VRES : 0;   // the dV pass reads no V
   __shared__ __attribute__((aligned(1024))) unsigned char smem[WALK_ONLY ? 16 : VRES + 2 * C::STAGE];
   __shared__ int cell_list[MAX_T];
   __shared__ int scratch4[4];
