@@ -22,5 +22,7 @@ Modules:
   visits     the expected set of visited (query cell, key cell) pairs
   dropout    the definition with dropout on P (Philox4x32-10 random bytes),
              forward and backward
+  fp8        the definition on the real values of OCP E4M3 inputs with
+             per-tensor descale factors
 """
-from . import attention, dropout, online, sparse, visits  # noqa: F401
+from . import attention, dropout, fp8, online, sparse, visits  # noqa: F401

@@ -142,6 +142,33 @@ def _bf16_round_finite(x: np.ndarray) -> np.ndarray:
     return (r << 16).view(np.float32)
 
 
+def quantize_e4m3(x):
+    """Per-tensor quantization to OCP E4M3 codes: descale = max|x| / 448 (1 if
+    x is all zero), codes = E4M3(x / descale) rounded to nearest even by
+    torch's float8_e4m3fn conversion.  Returns (uint8 codes, float32 descale)."""
+    import torch
+    x = np.asarray(x, np.float32)
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    descale = np.float32(amax / 448.0 if amax > 0 else 1.0)
+    y = np.clip(x / descale, -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, descale
+
+
+def draw_qkv_fp8(B, H, N, d, sigma=1.0, seed=0):
+    """Q, K, V as E4M3 codes with their descale factors: fp32 normals times
+    sigma from PCG64(seed) (drawn as draw_qkvdo draws Q, K, V), each tensor
+    quantized by quantize_e4m3.  Returns ((q8, dq), (k8, dk), (v8, dv))."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(3):
+        a = rng.standard_normal((B, H, N, d), dtype=np.float32)
+        if sigma != 1.0:
+            a *= np.float32(sigma)
+        out.append(quantize_e4m3(a))
+    return tuple(out)
+
+
 def draw_kv_len(B, lo, hi, seed):
     rng = np.random.Generator(np.random.PCG64(seed))
     return rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
