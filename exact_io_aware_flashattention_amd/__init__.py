@@ -23,7 +23,7 @@ CELL = 128
 
 EXPORTS = ("fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd_dkdv_workspace_bytes", "fa_bwd", "fa_bwd_preprocess",
            "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_splitkv_workspace_bytes",
-           "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv", "fa_debug_visits", "fa_status_str")
+           "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv", "fa_fwd_fp8", "fa_debug_visits", "fa_status_str")
 
 
 class FAError(RuntimeError):
@@ -62,6 +62,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fa_fwd_splitkv_workspace_bytes": [I, I, I, I, I, I],
         "fa_fwd_splitkv_num_splits": [I, I, I, I, I],
         "fa_fwd_splitkv": [P, P, P, P, P, I, I, I, I, I, F, I, P, I, I, P, S, P],
+        "fa_fwd_fp8": [P, P, P, P, P, I, I, I, I, F, I, P, P, F, F, F, P],
         "fa_debug_visits": [I, I, I, I, I, I, P, P, I, P, P, S, P],
         "fa_status_str": [I],
     }
@@ -155,6 +156,26 @@ def fa_fwd(q, k, v, o=None, lse=None, *, scale=None, causal=False, block_mask=No
     else:
         _call("fa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _scale(scale, d),
               int(bool(causal)), mb, kl, _dtype_code(q), _stream(stream))
+    return o, lse
+
+
+def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o=None, lse=None, *, scale=None, causal=False,
+               block_mask=None, kv_len=None, stream=None):
+    """O (bf16), lse for E4M3 inputs: q8, k8, v8 are uint8 [B,H,N,d] tensors of
+    OCP E4M3 codes whose real values are code * descale (one float per tensor)."""
+    import torch
+    B, H, N, d = _shape(q8)
+    for t in (q8, k8, v8):
+        if t.dtype != torch.uint8:
+            raise TypeError("FP8 inputs are uint8 tensors of E4M3 codes")
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    _check_like(q8, q8, k8, v8, o, lse, block_mask, kv_len)
+    mb, kl = _mask_args(block_mask, kv_len)
+    _call("fa_fwd_fp8", _ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, H, N, d, _scale(scale, d),
+          int(bool(causal)), mb, kl, float(q_descale), float(k_descale), float(v_descale), _stream(stream))
     return o, lse
 
 

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bf16.hip", "fa_split.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bf16.hip", "fa_split.hip", "fa_decode.hip", "fa_fp8.hip"]
 ARCH = "gfx950"
 
 COMMON = [

@@ -426,6 +426,33 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   return hip_status(p.decode ? fa::launch_fwd_decode_bf16(a, d, st) : fa::launch_fwd_splitkv_bf16(a, d, st));
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, const uint8_t* block_mask, const int32_t* kv_len, float q_descale,
+               float k_descale, float v_descale, void* stream) {
+  const Shape s{B, H, N, d, FA_BF16};
+  bool empty = false;
+  if (d != 64 && d != 128) return FA_ERR_SHAPE;
+  FA_TRY(check_shape(s, block_mask, &empty));
+  if (empty) return FA_OK;
+  FA_TRY(check_tensors({q, k, v, o}));
+  FA_TRY(check_rowstats({lse}));
+  FA_TRY(check_masks(block_mask, kv_len));
+  FA_TRY(check_scale(scale));
+  FA_TRY(check_scale(q_descale));
+  FA_TRY(check_scale(k_descale));
+  FA_TRY(check_scale(v_descale));
+  const float c = scale * q_descale * k_descale;
+  if (!isfinite(c) || !(c > 0.f)) return FA_ERR_ARG;
+  fa::AttnArgs a = make_args(s, c, causal, block_mask, kv_len);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out0 = o;
+  a.lse = lse;
+  a.v_descale = v_descale;
+  return hip_status(fa::launch_fwd_fp8(a, d, static_cast<hipStream_t>(stream)));
+}
+
 int fa_debug_visits(int which, int B, int H, int N, int d, int causal, const uint8_t* block_mask,
                     const int32_t* kv_len, int dtype, uint32_t* counts, void* workspace, size_t workspace_bytes,
                     void* stream) {

@@ -60,6 +60,9 @@ struct AttnArgs {
   int Nk, causal_off, nsplit, split_tiles;
   float* part_o;
   float* part_ml;
+  // FP8 forward: real V = E4M3 code * v_descale (the Q and K descales are
+  // folded into c)
+  float v_descale;
 };
 
 // Bytes of the dK/dV split workspace for N keys and head dimension d; the
@@ -83,6 +86,8 @@ hipError_t launch_split_plan(const AttnArgs& a, hipStream_t s);
 hipError_t launch_fwd_splitkv_bf16(const AttnArgs& a, int d, hipStream_t s);
 // The same for at most four queries per head (one wave per key range).
 hipError_t launch_fwd_decode_bf16(const AttnArgs& a, int d, hipStream_t s);
+// Forward on E4M3 Q, K, V (d = 64 or 128).
+hipError_t launch_fwd_fp8(const AttnArgs& a, int d, hipStream_t s);
 // Merge of the partial outputs a.part_o / a.part_ml into a.out0 and a.lse.
 hipError_t launch_splitkv_merge(const AttnArgs& a, int d, hipStream_t s);
 

@@ -244,6 +244,28 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    const int32_t* kv_len, int dtype, int num_splits,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Forward pass on 8-bit floating point inputs.  The pages name native FP8 as
+ * FlashAttention-3's way to halve memory traffic (datacamp "Penjelasan Flash
+ * Attention", Flash Attention 3, "Presisi FP8 native") without a format or
+ * scaling rule; this entry point reads it as:
+ *   q, k, v  [B,H,N,d] OCP E4M3 codes (uint8: 1 sign, 4 exponent bits with
+ *            bias 7, 3 mantissa bits, subnormals, S.1111.111 = NaN), each
+ *            tensor with one float32 descale: real value = decode(code) *
+ *            descale (q_descale, k_descale, v_descale finite and > 0);
+ *   o        [B,H,N,d] bf16 and lse [B,H,N] float32 as fa_fwd, of the real
+ *            values: O = softmax(scale (dq Q)(dk K)^T [masked]) (dv V).
+ * Both products run on the fp8 matrix core with fp32 accumulation; the
+ * probabilities are converted to E4M3 for the P V product (relative rounding
+ * up to 2^-4 per entry), while the running max, row sum and final division
+ * stay fp32.  d = 64 or 128; masks, errors and conventions as fa_fwd.  There
+ * is no FP8 backward pass.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               const uint8_t* block_mask, const int32_t* kv_len,
+               float q_descale, float k_descale, float v_descale, void* stream);
+
 /* Static, NUL-terminated name of a status code. */
 const char* fa_status_str(int status);
 

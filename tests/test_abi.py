@@ -177,6 +177,18 @@ def test_splitkv_plan_and_validation(lib):
     assert lib.fa_fwd_splitkv(P, P, P, P, P, 1, 2, 0, 500, 128, 0.1, 0, None, 0, 0, None, 0, None) == 0
 
 
+def test_fp8_validation(lib):
+    P = FAKE
+
+    def f8(d=128, scale=0.1, dq=1.0, dk=1.0, dv=1.0, q=P, N=128):
+        return lib.fa_fwd_fp8(q, P, P, P, P, 1, 1, N, d, scale, 0, None, None, dq, dk, dv, None)
+    assert f8(d=256) == 2 and f8(d=96) == 2            # d = 64 or 128
+    assert f8(q=None) == 1
+    assert f8(dq=0.0) == 7 and f8(dv=float("inf")) == 7 and f8(dk=-1.0) == 7
+    assert f8(scale=1e30, dq=1e30) == 7               # scale * dq * dk overflows float32
+    assert f8(N=0, q=None) == 0
+
+
 def test_debug_visits_validation(lib):
     assert lib.fa_debug_visits(3, 1, 1, 128, 64, 0, None, None, 0, FAKE, None, 0, None) == 7
     assert lib.fa_debug_visits(0, 1, 1, 128, 64, 0, None, None, 0, None, None, 0, None) == 1

@@ -1,0 +1,127 @@
+"""GPU parity of the FP8 forward (fa_fwd_fp8) against the FP8 oracle.
+
+Random inputs are compared with a bound derived from the arithmetic: the
+scores are exact (products of E4M3 values accumulated in fp32), while each
+probability p passes through E4M3 on its way into the P V product, which
+moves it by at most 2^-4 p (normal range) or 2^-10 (subnormal half-step).
+With P = p / l (l >= 1, the fp32 row sum) this gives per element
+    |dO_ij| <= 2^-4 sum_k P_ik |V_kj| + 2^-10 sum_k |V_kj| / l_i + 2^-8 |O_ij|
+(the last term for the bf16 output).  Two structured cases need no such
+slack and pin the operand layouts exactly: K = 0 under the causal mask makes
+every allowed probability exactly 1 (O_i = mean of V_0..V_i, so a wrong key
+order near the diagonal shows), and one-hot Q and K with a large scale make
+each query see only the keys of its own feature index."""
+import numpy as np
+import pytest
+
+from oracle import fp8 as ofp8
+from workloads import band_random_mask, draw_kv_len, draw_qkv_fp8
+
+from gpu_cases import host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_io_aware_flashattention_amd as fa
+    fa.load_library()
+
+
+def run(q8, k8, v8, dq, dk, dv, scale, causal=False, block_mask=None, kv_len=None):
+    import torch
+
+    import exact_io_aware_flashattention_amd as fa
+    t = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (q8, k8, v8)]
+    bm = None if block_mask is None else torch.from_numpy(block_mask).cuda()
+    kl = None if kv_len is None else torch.from_numpy(np.asarray(kv_len, np.int32)).cuda()
+    o, lse = fa.fa_fwd_fp8(*t, dq, dk, dv, scale=scale, causal=causal, block_mask=bm, kv_len=kl)
+    torch.cuda.synchronize()
+    return host(o), lse.cpu().numpy().astype(np.float64)
+
+
+def allowed(N, causal, bm, kv):
+    i, j = np.arange(N)[:, None], np.arange(N)[None, :]
+    ok = np.ones((N, N), bool)
+    if causal:
+        ok &= j <= i
+    if bm is not None:
+        ok &= bm[i // 128, j // 128] != 0
+    if kv is not None:
+        ok &= j < kv
+    return ok
+
+
+CASES = [
+    # B, H, N, d, causal, kv, mask
+    (1, 1, 1, 64, False, None, None),
+    (1, 2, 128, 128, False, None, None),
+    (2, 1, 300, 64, True, None, None),
+    (2, 2, 200, 128, False, "rand", None),
+    (1, 2, 513, 128, True, None, "band"),
+    (1, 1, 1000, 64, False, "rand", "band"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}N{}d{}{}{}{}".format(
+    c[0], c[1], c[2], c[3], "c" if c[4] else "", "k" if c[5] else "", "m" if c[6] else ""))
+def test_fp8_parity_within_e4m3_bound(case):
+    B, H, N, d, causal, kv, mask = case
+    (q8, dq), (k8, dk), (v8, dv) = draw_qkv_fp8(B, H, N, d, 1.0, 600 + N + d)
+    kv_len = draw_kv_len(B, 1, N, 610 + N) if kv else None
+    bm = band_random_mask(-(-N // 128), 620 + N, n_random=1) if mask else None
+    scale = 1 / np.sqrt(d)
+    say(f"fp8 parity {case} descales {dq:.4g} {dk:.4g} {dv:.4g}")
+    o, lse = run(q8, k8, v8, dq, dk, dv, scale, causal, bm, kv_len)
+    O, L = ofp8.forward(q8, k8, v8, dq, dk, dv, scale, causal=causal, block_mask=bm, kv_len=kv_len)
+    fin = np.isfinite(L)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.abs(lse[fin] - L[fin]).max(initial=0) <= 1e-3
+    assert np.all(o[~fin] == 0)
+    worst = 0.0
+    for b in range(B):
+        ok = allowed(N, causal, bm, None if kv_len is None else int(kv_len[b]))
+        for h in range(H):
+            Q, K, V = (ofp8.dequantize(c[b, h], s) for c, s in ((q8, dq), (k8, dk), (v8, dv)))
+            S = np.where(ok, scale * Q @ K.T, -np.inf)
+            m = S.max(axis=1, keepdims=True)
+            E = np.where(ok, np.exp(S - np.where(np.isfinite(m), m, 0.0)), 0.0)
+            l = np.maximum(E.sum(axis=1, keepdims=True), 1.0)
+            P = E / l
+            bound = 2.0 ** -4 * (P @ np.abs(V)) + 2.0 ** -10 * (ok @ np.abs(V)) / l + 2.0 ** -8 * np.abs(O[b, h])
+            err = np.abs(o[b, h] - O[b, h])
+            assert np.all(err <= bound + 1e-6), f"b{b} h{h}: {np.argwhere(err > bound + 1e-6)[:3]}"
+            worst = max(worst, float((err / (bound + 1e-6)).max()))
+    d_all = np.abs(o - O)
+    say(f"  max|dO| {d_all.max():.3e} mean {d_all.mean():.3e}, worst error / bound {worst:.3f}")
+
+
+def test_fp8_zero_keys_causal_prefix_mean():
+    """K = 0: every allowed score is 0 and every probability exactly 1, so
+    O_i = dv * mean(V_0 .. V_i) up to fp32 summation and the bf16 output."""
+    B, H, N, d = 1, 2, 300, 128
+    (q8, dq), _, (v8, dv) = draw_qkv_fp8(B, H, N, d, 1.0, 630)
+    k8 = np.zeros_like(q8)
+    o, lse = run(q8, k8, v8, dq, 1.0, dv, 0.1, causal=True)
+    V = ofp8.dequantize(v8, dv)
+    ref = np.cumsum(V, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+    assert np.all(np.abs(o - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5)
+    assert np.allclose(lse, np.log(np.arange(1, N + 1))[None, None, :], atol=1e-5)
+
+
+def test_fp8_one_hot_scores_select_matching_keys():
+    """Q_i and K_k one-hot at feature i mod d and k mod d (code 1.0), scale 20:
+    query i attends to the keys k = i mod d (probabilities of the others are
+    e^-20, flushed by E4M3), so O_i = mean of those V rows."""
+    B, H, N, d = 1, 1, 300, 128
+    onehot = np.zeros((B, H, N, d), np.uint8)
+    onehot[0, 0, np.arange(N), np.arange(N) % d] = 0x38
+    _, _, (v8, dv) = draw_qkv_fp8(B, H, N, d, 1.0, 640)
+    o, _ = run(onehot, onehot, v8, 1.0, 1.0, dv, 20.0)
+    V = ofp8.dequantize(v8, dv)[0, 0]
+    match = (np.arange(N)[:, None] % d) == (np.arange(N)[None, :] % d)
+    ref = (match @ V) / match.sum(axis=1, keepdims=True)
+    assert np.all(np.abs(o[0, 0] - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5)
