@@ -40,6 +40,7 @@ METRIC = "attention TFLOP/s fwd+bwd (bf16, 1 GPU) and % of MFMA bf16 peak, N=1Kâ
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
 PEAK_F32_TFLOPS = 157.3        # fp32 matrix peak
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 matrix peak
 
 
 def flops_fwd(B, H, N, d, causal, cell_frac=1.0):
@@ -263,6 +264,44 @@ def run_gpu_bench_splitkv(which, steps, warmup):
         "roofline": roofline}
 
 
+def run_gpu_bench_fp8(w, steps, warmup, inp):
+    """One step = one fa_fwd_fp8 call on the workload's Q, K, V quantized per
+    tensor to E4M3 (descale = amax / 448), bracketed by HIP events on the
+    launch stream."""
+    import torch
+
+    import exact_io_aware_flashattention_amd as fa
+    from workloads import quantize_e4m3
+
+    dev = torch.device("cuda:0")
+    (q8, dq), (k8, dk), (v8, dv) = (quantize_e4m3(inp[n]) for n in ("q", "k", "v"))
+    q, k, v = (torch.from_numpy(x).to(dev) for x in (q8, k8, v8))
+    B, H, N, d = q.shape
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fa.fa_fwd_fp8(q, k, v, float(dq), float(dk), float(dv), o, lse, scale=w.scale, causal=w.causal,
+                      stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o.float()).all())
+    call_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    return start.elapsed_time(end) / steps, call_ms, (B, H, N, d)
+
+
 COPY_BYTES = 256 << 20
 
 
@@ -421,6 +460,8 @@ def main():
                     help="time the step with dropout on P at this rate (fa_fwd_dropout + fa_bwd_dropout)")
     ap.add_argument("--splitkv", choices=("decode", "prefill"),
                     help="time the split-key forward (fa_fwd_splitkv) on a decode or chunked-prefill shape")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 forward (fa_fwd_fp8) on the workload's inputs quantized to E4M3")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg (profiling runs)")
     ap.add_argument("--cpu-baseline", action="store_true", help="run the CPU oracle leg for --workload other than 4")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -446,6 +487,22 @@ def main():
     from workloads import WORKLOADS, digest, make_inputs
     w = WORKLOADS[args.workload]
     inp = make_inputs(w)
+    if args.fp8:
+        step_ms, call_ms, (B, H, N, d) = run_gpu_bench_fp8(w, args.steps, args.warmup, inp)
+        F = workload_fwd_flops(w, inp)
+        tf = F / (call_ms * 1e-3) / 1e12
+        print(json.dumps({
+            "metric": "FP8 attention forward TFLOP/s (E4M3 inputs, 1 GPU)", "value": round(tf, 2),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "fp8-e4m3", "data": f"synthetic (seeded N(0, {w.sigma ** 2:g}) Q/K/V quantized per tensor "
+                                          f"to E4M3, inputs resident in HBM)",
+            "config": {"workload": f"workload {args.workload}, forward on E4M3 inputs", "B": B, "H": H, "N": N,
+                       "d": d, "causal": w.causal},
+            "roofline": {"bound": "mfma", "kernel": "fwd_fp8_kernel", "achieved": round(tf, 2),
+                         "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                         "traffic": None}}), flush=True)
+        return
     if args.dropout:
         step_ms, per, (B, H, N, d) = run_gpu_bench_dropout(w, args.steps, args.warmup, inp, args.dropout)
         F = workload_fwd_flops(w, inp)
