@@ -317,7 +317,7 @@ def copy_calibration():
     torch.cuda.synchronize()
 
 
-def cpu_baseline(w, inp, heads=2):
+def cpu_baseline(w, inp, heads=6):
     """fp64 oracle fwd + bwd on heads 0..heads-1 of batch entry 0 (all rows, all keys)."""
     import numpy as np
 
@@ -340,7 +340,7 @@ def cpu_baseline(w, inp, heads=2):
 
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "long_context_hbm_traffic.txt")
-KERNEL_SYMBOL = {"fwd": "fwd_bf16_kernel<128, 0>", "dkdv": "dkdv_bf16_kernel<128, 0, false>",
+KERNEL_SYMBOL = {"fwd": "fwd_bf16_kernel<128, 0>", "dkdv": "dkdv_bf16_kernel<128, 0, false, 0>",
                  "dq": "dq_bf16_kernel<128, 0>", "pre": "bwd_pre_kernel"}
 
 
