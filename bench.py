@@ -12,8 +12,8 @@ Each stage is bracketed by HIP events recorded on the stream the library
 launches on, so the per-kernel averages come from the timed steps themselves.
 The roofline object describes the kernel with the largest average time.
 
-cpu_baseline times the fp64 CPU oracle (forward + backward) on two heads of
-the same workload.
+cpu_baseline times the fp64 CPU oracle (forward + backward) on six heads of
+the same workload (about 10-30 s on one host).
 
 --workload K times one of the other workloads (1 tiny fp32, 2 GPT-2 shaped,
 3 BERT-shaped with key padding, 5 block-sparse 64K, 6 long context at head
