@@ -419,6 +419,10 @@ dkdv_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < C::SSTEPS; ++s)
       kf[s] = myk < N ? ld16(Kg + (size_t)myk * D + s * 16 + 8 * h) : u32x4{0, 0, 0, 0};
+    // d = 64: the wave's V rows stay in registers (16 per lane) after the
+    // first tile, instead of being read from LDS for every 32 queries
+    constexpr bool VREG = D == 64 && DO_DK;
+    u32x4 vfr[VREG ? C::SSTEPS : 1];
     f32x16 dk[DO_DK ? C::NB : 1], dv[DO_DV ? C::NB : 1];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
@@ -453,6 +457,12 @@ dkdv_bf16_kernel(AttnArgs a) {
         stats[C::BQ + tid] = st_d;
       }
       __syncthreads();
+      if constexpr (VREG) {
+        if (it == 0) {   // the wave's V rows, resident in LDS since the first barrier
+#pragma unroll
+          for (int k = 0; k < C::SSTEPS; ++k) vfr[k] = row_chunk<D>(Vs, wave * 32 + l32, 2 * k + h);
+        }
+      }
       if (it + 1 < walk.ntiles) issue(it + 1);
       const int q0 = walk.tile_start(it);
       const unsigned char* Qs = st;
@@ -470,7 +480,7 @@ dkdv_bf16_kernel(AttnArgs a) {
           mma(s, as_bf16x8(row_chunk<D>(Qs, 32 * qs + l32, 2 * k + h)), as_bf16x8(kf[k]));
           if constexpr (DO_DK)
             mma(dp, as_bf16x8(row_chunk<D>(dOs, 32 * qs + l32, 2 * k + h)),
-                as_bf16x8(row_chunk<D>(Vs, wave * 32 + l32, 2 * k + h)));
+                as_bf16x8(VREG ? vfr[k] : row_chunk<D>(Vs, wave * 32 + l32, 2 * k + h)));
         }
         // P = exp2(s c - lse log2 e), dS = P (dP - delta); register r <-> query
         // q0 + 32 qs + acc_row(r, h).  On edge tiles an entry is masked iff the
