@@ -92,6 +92,19 @@ def head_forward(Q, K, V, scale, bh, t, seed, rows=None, causal=False, block_mas
     return (P * Z) @ V, lse
 
 
+def _row_grads(Q, K, V, dO, scale, bh, t, seed, rows, causal, block_mask, kv_len):
+    """P * Z and dS of the given query rows (every term of a row is row-local:
+    its softmax, its keep pattern, dP = (dO V^T) * Z and D = sum_j P dP)."""
+    keys = np.arange(K.shape[0])
+    S = scale * (Q[rows] @ K.T)
+    S = np.where(allowed(rows, K.shape[0], causal, block_mask, kv_len), S, -np.inf)
+    P, _ = _probs(S)
+    Z = keep_scale(bh, rows, keys, t, seed)
+    dP = (dO[rows] @ V.T) * Z
+    D = (P * dP).sum(axis=1)
+    return P * Z, P * (dP - D[:, None])
+
+
 def head_backward(Q, K, V, dO, scale, bh, t, seed, causal=False, block_mask=None, kv_len=None,
                   row_block=1024):
     """One head: dQ, dK, dV with dropout, by the chain rule in the module docstring."""
@@ -101,20 +114,22 @@ def head_backward(Q, K, V, dO, scale, bh, t, seed, causal=False, block_mask=None
     dO = np.asarray(dO, np.float64)
     N = Q.shape[0]
     dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
-    keys = np.arange(K.shape[0])
     for r0 in range(0, N, row_block):
         rows = np.arange(r0, min(N, r0 + row_block))
-        S = scale * (Q[rows] @ K.T)
-        S = np.where(allowed(rows, K.shape[0], causal, block_mask, kv_len), S, -np.inf)
-        P, _ = _probs(S)
-        Z = keep_scale(bh, rows, keys, t, seed)
-        dV += (P * Z).T @ dO[rows]
-        dP = (dO[rows] @ V.T) * Z
-        D = (P * dP).sum(axis=1)
-        dS = P * (dP - D[:, None])
+        PZ, dS = _row_grads(Q, K, V, dO, scale, bh, t, seed, rows, causal, block_mask, kv_len)
+        dV += PZ.T @ dO[rows]
         dQ[rows] = scale * (dS @ K)
         dK += scale * (dS.T @ Q[rows])
     return dQ, dK, dV
+
+
+def head_backward_rows(Q, K, V, dO, scale, bh, t, seed, rows, causal=False, block_mask=None, kv_len=None):
+    """dQ[rows] of one head with dropout (for long sequences, where the full
+    backward would hold N x N arrays)."""
+    Q, K, V, dO = (np.asarray(x, np.float64) for x in (Q, K, V, dO))
+    rows = np.asarray(rows, np.int64)
+    _, dS = _row_grads(Q, K, V, dO, scale, bh, t, seed, rows, causal, block_mask, kv_len)
+    return scale * (dS @ K)
 
 
 def forward(q, k, v, scale, t, seed, causal=False, block_mask=None, kv_len=None):

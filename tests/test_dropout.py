@@ -162,3 +162,25 @@ def test_zero_rate_equals_plain():
     o2, l2 = fa.fa_fwd(tq, tk, tv, causal=True, dropout_p=0.001, seed=9)   # rounds to t = 0
     torch.cuda.synchronize()
     assert torch.equal(o0, o1) and torch.equal(o0, o2) and torch.equal(l0, l2)
+
+
+def test_dropout_full_size_sampled():
+    """The long-context workload (B1 H16 N16384 d128 causal) with the rate and
+    seed bench.py --dropout times (t = 26, seed 2024): sampled rows of O, lse
+    and dQ on the first and last head against the dropout oracle."""
+    from workloads import WORKLOADS, make_inputs
+    w = WORKLOADS[4]
+    inp = make_inputs(w)
+    t, seed, N = 26, 2024, w.N
+    say(f"dropout full size: t={t} seed={seed}")
+    out = run(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, t, seed, causal=True)
+    rng = np.random.Generator(np.random.PCG64(380))
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, N // 2, N - 1], rng.integers(0, N, 34)]))
+    keep_frac = 1 - t / 256
+    for h in (0, w.H - 1):
+        Q, K, V, dO = (inp[n][0, h] for n in ("q", "k", "v", "do"))
+        O, lse = odrop.head_forward(Q, K, V, w.scale, h, t, seed, rows=rows, causal=True)
+        compare_forward(out["o"][0, h][rows] * keep_frac, out["lse"][0, h][rows], O * keep_frac, lse, "bf16",
+                        f"dropout full h{h}")
+        dQ = odrop.head_backward_rows(Q, K, V, dO, w.scale, h, t, seed, rows, causal=True)
+        compare_grad(out["dq"][0, h][rows], dQ, "bf16", f"dropout full h{h} dq rows")

@@ -125,3 +125,32 @@ def test_fp8_one_hot_scores_select_matching_keys():
     match = (np.arange(N)[:, None] % d) == (np.arange(N)[None, :] % d)
     ref = (match @ V) / match.sum(axis=1, keepdims=True)
     assert np.all(np.abs(o[0, 0] - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5)
+
+
+def test_fp8_full_size_sampled():
+    """The long-context workload's inputs quantized per tensor, as bench.py
+    --fp8 times them (B1 H16 N16384 d128 causal): sampled rows of O and lse on
+    the first and last head, within the E4M3 bound."""
+    from oracle import attention
+    from workloads import WORKLOADS, make_inputs, quantize_e4m3
+    w = WORKLOADS[4]
+    inp = make_inputs(w)
+    (q8, dq), (k8, dk), (v8, dv) = (quantize_e4m3(inp[n]) for n in ("q", "k", "v"))
+    say("fp8 full size")
+    o, lse = run(q8, k8, v8, dq, dk, dv, w.scale, causal=True)
+    N = w.N
+    rng = np.random.Generator(np.random.PCG64(650))
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, N // 2, N - 1], rng.integers(0, N, 34)]))
+    for h in (0, w.H - 1):
+        Q, K, V = (ofp8.dequantize(c[0, h], s) for c, s in ((q8, dq), (k8, dk), (v8, dv)))
+        O, L = attention.head_forward(Q, K, V, w.scale, rows, causal=True)
+        assert np.abs(lse[0, h][rows] - L).max() <= 1e-3
+        ok = np.arange(N)[None, :] <= rows[:, None]
+        S = np.where(ok, w.scale * Q[rows] @ K.T, -np.inf)
+        E = np.exp(S - S.max(axis=1, keepdims=True))
+        l = E.sum(axis=1, keepdims=True)
+        P = E / l
+        bound = 2.0 ** -4 * (P @ np.abs(V)) + 2.0 ** -10 * (ok @ np.abs(V)) / l + 2.0 ** -8 * np.abs(O)
+        err = np.abs(o[0, h][rows] - O)
+        say(f"  h{h}: max|dO| {err.max():.3e}, worst error / bound {(err / (bound + 1e-6)).max():.3f}")
+        assert np.all(err <= bound + 1e-6)

@@ -139,3 +139,14 @@ def test_dropout_is_unbiased_in_expectation():
         acc += dropout.head_forward(q, k, v, 0.5, 0, 128, 1000 + s)[0]
     # per entry the estimate has standard error < max|V| / sqrt(n) (keep rate 1/2, scale 2)
     assert np.abs(acc / n - O0).max() < 5 * np.abs(v).max() / np.sqrt(n)
+
+
+def test_dq_rows_equal_the_full_backward():
+    """head_backward_rows (sampled rows, for long sequences) gives the same dQ
+    rows as the full backward, under each mask setting."""
+    q, k, v, do = small(N=40, d=6, seed=46)
+    rows = np.array([0, 3, 17, 39])
+    for kw in (dict(), dict(causal=True), dict(kv_len=21)):
+        full = dropout.head_backward(q, k, v, do, 0.4, 3, 90, 77, **kw)[0]
+        part = dropout.head_backward_rows(q, k, v, do, 0.4, 3, 90, 77, rows, **kw)
+        assert np.allclose(part, full[rows], rtol=1e-13, atol=1e-13)
