@@ -193,19 +193,20 @@ def splitkv_pairs(Nq, Nk, causal):
     return sum(max(0, min(Nk, i + Nk - Nq + 1)) for i in range(Nq))
 
 
-def splitkv_alg(w):
+def splitkv_alg(w, fp8kv=False):
     """Algorithmic flops (S and PV products over allowed pairs) and compulsory
     HBM bytes (Q, K, V read once; O and lse written once) of one split-key
-    forward call."""
+    forward call; fp8kv: K and V are one byte per feature."""
     B, H, Nq, Nk, d = w["B"], w["H"], w["Nq"], w["Nk"], w["d"]
     flops = 4.0 * B * H * splitkv_pairs(Nq, Nk, w["causal"]) * d
-    nbytes = 2 * B * H * (2 * Nq + 2 * Nk) * d + 4 * B * H * Nq
+    nbytes = B * H * (2 * 2 * Nq + (1 if fp8kv else 2) * 2 * Nk) * d + 4 * B * H * Nq
     return flops, nbytes
 
 
-def run_gpu_bench_splitkv(which, steps, warmup):
+def run_gpu_bench_splitkv(which, steps, warmup, fp8kv=False):
     """One step = one fa_fwd_splitkv call (range kernel + merge), bracketed by
-    HIP events on the launch stream."""
+    HIP events on the launch stream; fp8kv: fa_fwd_splitkv_fp8kv with K and V
+    quantized per tensor to E4M3 (decode only)."""
     import torch
 
     import exact_io_aware_flashattention_amd as fa
@@ -216,6 +217,10 @@ def run_gpu_bench_splitkv(which, steps, warmup):
     qa, ka, va = draw_split_qkv(B, H, Nq, Nk, d, w["sigma"], w["seed"])
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(a).to(dev, torch.bfloat16) for a in (qa, ka, va))
+    if fp8kv:
+        from workloads import quantize_e4m3
+        (k8, dk), (v8, dv) = quantize_e4m3(ka), quantize_e4m3(va)
+        k, v = torch.from_numpy(k8).to(dev), torch.from_numpy(v8).to(dev)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
     ws = torch.empty(fa.fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d), dtype=torch.uint8, device=dev)
@@ -223,7 +228,11 @@ def run_gpu_bench_splitkv(which, steps, warmup):
     scale = 1.0 / math.sqrt(d)
 
     def step():
-        fa.fa_fwd_splitkv(q, k, v, o, lse, scale=scale, causal=w["causal"], workspace=ws, stream=stream)
+        if fp8kv:
+            fa.fa_fwd_splitkv_fp8kv(q, k, v, float(dk), float(dv), o, lse, scale=scale, causal=w["causal"],
+                                    workspace=ws, stream=stream)
+        else:
+            fa.fa_fwd_splitkv(q, k, v, o, lse, scale=scale, causal=w["causal"], workspace=ws, stream=stream)
 
     for _ in range(warmup):
         step()
@@ -239,7 +248,7 @@ def run_gpu_bench_splitkv(which, steps, warmup):
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all())
     call_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
-    flops, nbytes = splitkv_alg(w)
+    flops, nbytes = splitkv_alg(w, fp8kv)
     nsplit = fa.fa_fwd_splitkv_num_splits(B, H, Nq, Nk, 0)
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     tf, gbs = flops / (call_ms * 1e-3) / 1e12, nbytes / (call_ms * 1e-3) / 1e9
@@ -248,7 +257,8 @@ def run_gpu_bench_splitkv(which, steps, warmup):
         roofline = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
     else:
-        metric, value, unit = "split-key forward GB/s of compulsory HBM traffic (bf16, 1 GPU)", gbs, "GB/s"
+        metric, value, unit = (f"split-key forward GB/s of compulsory HBM traffic "
+                               f"({'bf16 queries, E4M3 K/V' if fp8kv else 'bf16'}, 1 GPU)", gbs, "GB/s")
         roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(gbs / PEAK_HBM_GBS, 4)}
     roofline.update({"kernel": "fa_fwd_splitkv call (range kernel + merge)", "traffic": None,
@@ -256,9 +266,10 @@ def run_gpu_bench_splitkv(which, steps, warmup):
     return {
         "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(start.elapsed_time(end) / steps, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16",
+        "vs_baseline": None, "dtype": "bf16 queries, E4M3 K/V" if fp8kv else "bf16",
         "data": f"synthetic (seeded N(0, {w['sigma'] ** 2:g}) Q/K/V, inputs resident in HBM)",
-        "config": {"workload": w["desc"], "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "causal": w["causal"],
+        "config": {"workload": w["desc"] + (", K/V cache in E4M3" if fp8kv else ""), "B": B, "H": H, "Nq": Nq,
+                   "Nk": Nk, "d": d, "causal": w["causal"],
                    "num_splits": nsplit, "input_sha256": digest(qa, ka, va)},
         "call_ms": round(call_ms, 4), "tflops": round(tf, 2), "hbm_gbs": round(gbs, 1),
         "roofline": roofline}
@@ -481,7 +492,10 @@ def main():
         sweep(args.steps, args.warmup)
         return
     if args.splitkv:
-        print(json.dumps(run_gpu_bench_splitkv(args.splitkv, args.steps, args.warmup)), flush=True)
+        if args.fp8 and args.splitkv != "decode":
+            print("--fp8 with --splitkv applies to decode only (an E4M3 key/value cache)", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(run_gpu_bench_splitkv(args.splitkv, args.steps, args.warmup, fp8kv=args.fp8)), flush=True)
         return
 
     from workloads import WORKLOADS, digest, make_inputs

@@ -23,7 +23,7 @@ CELL = 128
 
 EXPORTS = ("fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd_dkdv_workspace_bytes", "fa_bwd", "fa_bwd_preprocess",
            "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_splitkv_workspace_bytes",
-           "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv", "fa_fwd_fp8", "fa_debug_visits", "fa_status_str")
+           "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv", "fa_fwd_splitkv_fp8kv", "fa_fwd_fp8", "fa_debug_visits", "fa_status_str")
 
 
 class FAError(RuntimeError):
@@ -63,6 +63,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fa_fwd_splitkv_num_splits": [I, I, I, I, I],
         "fa_fwd_splitkv": [P, P, P, P, P, I, I, I, I, I, F, I, P, I, I, P, S, P],
         "fa_fwd_fp8": [P, P, P, P, P, I, I, I, I, F, I, P, P, F, F, F, P],
+        "fa_fwd_splitkv_fp8kv": [P, P, P, P, P, I, I, I, I, I, F, I, P, F, F, I, P, S, P],
         "fa_debug_visits": [I, I, I, I, I, I, P, P, I, P, P, S, P],
         "fa_status_str": [I],
     }
@@ -156,6 +157,30 @@ def fa_fwd(q, k, v, o=None, lse=None, *, scale=None, causal=False, block_mask=No
     else:
         _call("fa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _scale(scale, d),
               int(bool(causal)), mb, kl, _dtype_code(q), _stream(stream))
+    return o, lse
+
+
+def fa_fwd_splitkv_fp8kv(q, k8, v8, k_descale, v_descale, o=None, lse=None, *, scale=None, causal=False,
+                         kv_len=None, num_splits=0, workspace=None, stream=None):
+    """Decoding (at most 4 bf16 queries [B,H,Nq,d]) against E4M3 K and V codes
+    (uint8 [B,H,Nk,d]; real value = code * descale), keys split over ranges
+    as fa_fwd_splitkv."""
+    import torch
+    B, H, Nq, d = _shape(q)
+    Bk, Hk, Nk, dk = _shape(k8)
+    if (Bk, Hk, dk) != (B, H, d) or tuple(v8.shape) != tuple(k8.shape):
+        raise ValueError("k8 and v8 must be [B, H, Nk, d] with q's B, H and d")
+    if k8.dtype != torch.uint8 or v8.dtype != torch.uint8:
+        raise TypeError("K and V are uint8 tensors of E4M3 codes")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_like(q, q, k8, v8, o, lse, kv_len)
+    ws, nbytes = _workspace(workspace, fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits), q.device)
+    _call("fa_fwd_splitkv_fp8kv", _ptr(q), _ptr(k8) if Nk else None, _ptr(v8) if Nk else None, _ptr(o), _ptr(lse),
+          B, H, Nq, Nk, d, _scale(scale, d), int(bool(causal)), _ptr(kv_len), float(k_descale), float(v_descale),
+          int(num_splits), _ptr(ws), nbytes, _stream(stream))
     return o, lse
 
 

@@ -426,6 +426,44 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   return hip_status(p.decode ? fa::launch_fwd_decode_bf16(a, d, st) : fa::launch_fwd_splitkv_bf16(a, d, st));
 }
 
+int fa_fwd_splitkv_fp8kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                         int Nk, int d, float scale, int causal, const int32_t* kv_len, float k_descale,
+                         float v_descale, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  FA_TRY(check_splitkv_shape(B, H, Nq, Nk, d, FA_BF16, &empty));
+  if (empty) return FA_OK;
+  if (Nq > kDecodeMaxQ) return FA_ERR_SHAPE;
+  KvPlan p;
+  FA_TRY(splitkv_plan(B, H, Nq, Nk, num_splits, &p));
+  FA_TRY(check_tensors({q, o}));
+  if (Nk > 0) FA_TRY(check_tensors({k, v}));
+  FA_TRY(check_rowstats({lse}));
+  FA_TRY(check_masks(nullptr, kv_len));
+  FA_TRY(check_scale(scale));
+  FA_TRY(check_scale(k_descale));
+  FA_TRY(check_scale(v_descale));
+  const float c = scale * k_descale;
+  if (!isfinite(c) || !(c > 0.f)) return FA_ERR_ARG;
+  if (!workspace) return FA_ERR_NULL;
+  if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+  if (workspace_bytes < splitkv_bytes(B, H, Nq, Nk, d, num_splits)) return FA_ERR_WORKSPACE;
+  fa::AttnArgs a = make_args(Shape{B, H, Nq, d, FA_BF16}, c, causal, nullptr, kv_len);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out0 = o;
+  a.lse = lse;
+  a.Nk = Nk;
+  a.causal_off = Nk - Nq;
+  a.nsplit = p.nsplit;
+  a.split_tiles = p.tps;
+  a.v_descale = v_descale;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                       splitkv_o_bytes(B, H, Nq, d, p.nsplit));
+  return hip_status(fa::launch_fwd_decode_e4m3kv(a, d, static_cast<hipStream_t>(stream)));
+}
+
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                float scale, int causal, const uint8_t* block_mask, const int32_t* kv_len, float q_descale,
                float k_descale, float v_descale, void* stream) {

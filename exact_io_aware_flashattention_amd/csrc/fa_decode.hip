@@ -37,12 +37,15 @@
 namespace fa {
 namespace {
 
-template <int D>
+// F8: K and V are E4M3 codes (one byte per feature) instead of bf16.
+template <int D, bool F8>
 struct DecCfg {
-  static constexpr int LPR = D / 8;      // lanes per key row (16 bytes each)
-  static constexpr int KPI = 64 / LPR;   // key rows per load instruction
-  static constexpr int G = 8;            // load instructions per block and tensor
-  static constexpr int KB = G * KPI;     // keys per block: 16 (d = 256), 32 (d = 128), 64 (d = 64)
+  static constexpr int RB = F8 ? D : 2 * D;   // bytes per key row
+  static constexpr int EPL = F8 ? 16 : 8;     // features per lane (one 16-byte chunk)
+  static constexpr int LPR = RB / 16;         // lanes per key row
+  static constexpr int KPI = 64 / LPR;        // key rows per load instruction
+  static constexpr int G = 8;                 // load instructions per block and tensor
+  static constexpr int KB = G * KPI;          // keys per block: 16 .. 64 (bf16), 32 .. 128 (E4M3)
 };
 
 // Cache policy of the K and V loads: non-temporal (each byte is read once).
@@ -91,9 +94,27 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
   return acc;
 }
 
-template <int D, int NQ>
+// q . k over one lane's 16 E4M3 features (16 c .. 16 c + 15) of a key row:
+// each byte pair becomes a bf16 pair exactly (E4M3 values are bf16 values)
+// and meets the matching bf16 pair of the query, q[u] holding features
+// 16 c + 8 u .. + 7.
+__device__ __forceinline__ float dot16_e4m3(u32x4 k, const u32x4 (&q)[2], float acc) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t kw = k[w];
+    const uint32_t q0 = q[w >> 1][2 * (w & 1)], q1 = q[w >> 1][2 * (w & 1) + 1];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw, 1.0f, false),
+                                          __builtin_bit_cast(b2, q0), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw, 1.0f, true),
+                                          __builtin_bit_cast(b2, q1), acc, false);
+  }
+  return acc;
+}
+
+template <int D, int NQ, bool F8>
 __global__ __launch_bounds__(NT) void decode_kernel(AttnArgs a) {
-  using C = DecCfg<D>;
+  using C = DecCfg<D, F8>;
   const int lane = threadIdx.x & 63;
   const long long gw = (long long)blockIdx.x * (NT / 64) + wave_id();   // wave-uniform
   const int BH = a.B * a.H, S = a.nsplit;
@@ -115,13 +136,21 @@ __global__ __launch_bounds__(NT) void decode_kernel(AttnArgs a) {
   }
   const int R = a.split_tiles * 64;
   const int k_lo = split * R, k_hi = min(k_lo + R, lim_hi);
+  // A block (KB keys) can reach past the range when KB > 64 (E4M3 at d = 64):
+  // keys at or past k_hi read as zeros and must be masked like disallowed keys.
+  lim_lo = min(lim_lo, k_hi);
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) lim[i] = min(lim[i], k_hi);
 
   const bf16* Qh = reinterpret_cast<const bf16*>(a.q) + (size_t)bh * Nq * D;
-  u32x4 qv[NQ];
+  u32x4 qv[NQ][C::EPL / 8];   // features EPL c .. EPL c + EPL - 1 of each query
 #pragma unroll
-  for (int i = 0; i < NQ; ++i) qv[i] = i < Nq ? ld16(Qh + (size_t)i * D + 8 * c) : u32x4{0, 0, 0, 0};
+  for (int i = 0; i < NQ; ++i)
+#pragma unroll
+    for (int u = 0; u < C::EPL / 8; ++u)
+      qv[i][u] = i < Nq ? ld16(Qh + (size_t)i * D + C::EPL * c + 8 * u) : u32x4{0, 0, 0, 0};
 
-  float m_run[NQ], neg_mu[NQ], thr[NQ], l_run[NQ], acc[NQ][8];
+  float m_run[NQ], neg_mu[NQ], thr[NQ], l_run[NQ], acc[NQ][C::EPL];
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
     m_run[i] = neg_inf();
@@ -129,29 +158,31 @@ __global__ __launch_bounds__(NT) void decode_kernel(AttnArgs a) {
     thr[i] = neg_inf();
     l_run[i] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+    for (int e = 0; e < C::EPL; ++e) acc[i][e] = 0.f;
   }
   const float inv_c = 1.f / a.c;
 
   if (k_lo < k_hi) {
-    const size_t head = (size_t)bh * NK * D;
-    const uint32_t bytes = (uint32_t)k_hi * D * 2;
+    const size_t head = (size_t)bh * NK * C::RB;   // bytes
+    const uint32_t bytes = (uint32_t)k_hi * C::RB;
     const __amdgpu_buffer_rsrc_t rsK = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>(reinterpret_cast<const bf16*>(a.k) + head), (short)0, (int)bytes, 0x00020000);
+        const_cast<unsigned char*>(reinterpret_cast<const unsigned char*>(a.k) + head), (short)0, (int)bytes,
+        0x00020000);
     const __amdgpu_buffer_rsrc_t rsV = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16*>(reinterpret_cast<const bf16*>(a.v) + head), (short)0, (int)bytes, 0x00020000);
-    const int voff0 = (r * D + 8 * c) * 2;
+        const_cast<unsigned char*>(reinterpret_cast<const unsigned char*>(a.v) + head), (short)0, (int)bytes,
+        0x00020000);
+    const int voff0 = r * C::RB + 16 * c;
 
     u32x4 kA[C::G], vA[C::G], kB[C::G], vB[C::G];
     auto load = [&](u32x4 (&kb)[C::G], u32x4 (&vb)[C::G], int j0) {
 #pragma unroll
       for (int g = 0; g < C::G; ++g) {
-        const int off = voff0 + (j0 + g * C::KPI) * D * 2;
+        const int off = voff0 + (j0 + g * C::KPI) * C::RB;
         kb[g] = __builtin_amdgcn_raw_buffer_load_b128(rsK, off, 0, kStream);
       }
 #pragma unroll
       for (int g = 0; g < C::G; ++g) {
-        const int off = voff0 + (j0 + g * C::KPI) * D * 2;
+        const int off = voff0 + (j0 + g * C::KPI) * C::RB;
         vb[g] = __builtin_amdgcn_raw_buffer_load_b128(rsV, off, 0, kStream);
       }
     };
@@ -162,7 +193,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(AttnArgs a) {
       for (int i = 0; i < NQ; ++i) {
 #pragma unroll
         for (int g = 0; g < C::G; ++g) {
-          s[i][g] = row_sum<C::LPR>(dot8(kb[g], qv[i], 0.f));
+          if constexpr (F8)
+            s[i][g] = row_sum<C::LPR>(dot16_e4m3(kb[g], qv[i], 0.f));
+          else
+            s[i][g] = row_sum<C::LPR>(dot8(kb[g], qv[i][0], 0.f));
           if (!full && j0 + g * C::KPI + r >= lim[i]) s[i][g] = neg_inf();
         }
         float mx = s[i][0];
@@ -174,7 +208,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(AttnArgs a) {
           const float alpha = (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
           l_run[i] *= alpha;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[i][e] *= alpha;
+          for (int e = 0; e < C::EPL; ++e) acc[i][e] *= alpha;
           m_run[i] = m_new;
           const bool live = m_new != neg_inf();
           neg_mu[i] = live ? -m_new : 0.f;
@@ -183,20 +217,29 @@ __global__ __launch_bounds__(NT) void decode_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int g = 0; g < C::G; ++g) {
-        float v[8];
+        float v[C::EPL];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t w = vb[g][e];   // bf16 features 8c + 2e (low half), 8c + 2e + 1 (high half)
-          const uint32_t lo = w << 16, hi = w & 0xffff0000u;
-          v[2 * e] = __builtin_bit_cast(float, lo);
-          v[2 * e + 1] = __builtin_bit_cast(float, hi);
+          const uint32_t w = vb[g][e];
+          if constexpr (F8) {   // E4M3 features 16 c + 4 e .. + 3
+            typedef float f2 __attribute__((ext_vector_type(2)));
+            const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+            v[4 * e] = lo[0];
+            v[4 * e + 1] = lo[1];
+            v[4 * e + 2] = hi[0];
+            v[4 * e + 3] = hi[1];
+          } else {   // bf16 features 8c + 2e (low half), 8c + 2e + 1 (high half)
+            const uint32_t lo = w << 16, hi = w & 0xffff0000u;
+            v[2 * e] = __builtin_bit_cast(float, lo);
+            v[2 * e + 1] = __builtin_bit_cast(float, hi);
+          }
         }
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i][g], a.c, neg_mu[i]));
           l_run[i] += p;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[i][e] = __builtin_fmaf(p, v[e], acc[i][e]);
+          for (int e = 0; e < C::EPL; ++e) acc[i][e] = __builtin_fmaf(p, v[e], acc[i][e]);
         }
       }
     };
@@ -222,41 +265,53 @@ __global__ __launch_bounds__(NT) void decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int o = C::LPR; o < 64; o <<= 1)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[i][e] += __shfl_xor(acc[i][e], o);
+      for (int e = 0; e < C::EPL; ++e) acc[i][e] += __shfl_xor(acc[i][e], o);
     const float l_tot = wave_sum(c == 0 ? l_run[i] : 0.f);
     if (i < Nq) {
       const size_t prow = ((size_t)split * BH + bh) * Nq + i;
       if (r == 0) {
-        float* po = a.part_o + prow * D + 8 * c;
-        *reinterpret_cast<f32x4*>(po) = f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
-        *reinterpret_cast<f32x4*>(po + 4) = f32x4{acc[i][4], acc[i][5], acc[i][6], acc[i][7]};
+        // the value descale (E4M3 V) is applied here, so the merge is shared
+        const float vs = F8 ? a.v_descale : 1.f;
+        float* po = a.part_o + prow * D + C::EPL * c;
+#pragma unroll
+        for (int e = 0; e < C::EPL; e += 4)
+          *reinterpret_cast<f32x4*>(po + e) =
+              f32x4{acc[i][e] * vs, acc[i][e + 1] * vs, acc[i][e + 2] * vs, acc[i][e + 3] * vs};
       }
       if (lane == 0) *reinterpret_cast<float2*>(a.part_ml + 2 * prow) = float2{m_run[i], l_tot};
     }
   }
 }
 
-template <int D, int NQ>
+template <int D, int NQ, bool F8>
 hipError_t launch_decode(const AttnArgs& a, hipStream_t s) {
   const long long waves = (long long)a.B * a.H * a.nsplit;
   const long long nwg = (waves + NT / 64 - 1) / (NT / 64);
-  hipLaunchKernelGGL((decode_kernel<D, NQ>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<D, NQ, F8>), dim3((unsigned)nwg), dim3(NT), 0, s, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_splitkv_merge(a, D, s);
 }
 
-template <int D>
+template <int D, bool F8>
 hipError_t launch_decode_d(const AttnArgs& a, hipStream_t s) {
-  if (a.N <= 1) return launch_decode<D, 1>(a, s);
-  if (a.N <= 2) return launch_decode<D, 2>(a, s);
-  return launch_decode<D, 4>(a, s);
+  if (a.N <= 1) return launch_decode<D, 1, F8>(a, s);
+  if (a.N <= 2) return launch_decode<D, 2, F8>(a, s);
+  return launch_decode<D, 4, F8>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_decode_bf16(const AttnArgs& a, int d, hipStream_t s) {
-  return d == 64 ? launch_decode_d<64>(a, s) : d == 256 ? launch_decode_d<256>(a, s) : launch_decode_d<128>(a, s);
+  return d == 64    ? launch_decode_d<64, false>(a, s)
+         : d == 256 ? launch_decode_d<256, false>(a, s)
+                    : launch_decode_d<128, false>(a, s);
+}
+
+hipError_t launch_fwd_decode_e4m3kv(const AttnArgs& a, int d, hipStream_t s) {
+  return d == 64    ? launch_decode_d<64, true>(a, s)
+         : d == 256 ? launch_decode_d<256, true>(a, s)
+                    : launch_decode_d<128, true>(a, s);
 }
 
 }  // namespace fa

@@ -86,6 +86,8 @@ hipError_t launch_split_plan(const AttnArgs& a, hipStream_t s);
 hipError_t launch_fwd_splitkv_bf16(const AttnArgs& a, int d, hipStream_t s);
 // The same for at most four queries per head (one wave per key range).
 hipError_t launch_fwd_decode_bf16(const AttnArgs& a, int d, hipStream_t s);
+// Decoding against E4M3 K and V (bf16 queries; a.c holds the K descale).
+hipError_t launch_fwd_decode_e4m3kv(const AttnArgs& a, int d, hipStream_t s);
 // Forward on E4M3 Q, K, V (d = 64 or 128).
 hipError_t launch_fwd_fp8(const AttnArgs& a, int d, hipStream_t s);
 // Merge of the partial outputs a.part_o / a.part_ml into a.out0 and a.lse.

@@ -245,6 +245,25 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decoding against an 8-bit key/value cache: fa_fwd_splitkv for Nq <= 4 bf16
+ * queries with K and V stored as OCP E4M3 codes ([B,H,Nk,d] uint8, real
+ * value = decode(code) * k_descale or * v_descale; the format as for
+ * fa_fwd_fp8 below).  Reading K and V is the whole cost of decoding, so the
+ * 8-bit cache halves it -- the memory-traffic saving the pages give for FP8
+ * (datacamp "Penjelasan Flash Attention", Flash Attention 3, "Presisi FP8
+ * native").  Scores are bf16 query x E4M3 key products (each E4M3 value is
+ * exactly a bf16 value) with fp32 accumulation; probabilities and the P V
+ * accumulation stay fp32.  Arguments, masks, splits, workspace
+ * (fa_fwd_splitkv_workspace_bytes) and errors as fa_fwd_splitkv;
+ * FA_ERR_SHAPE if Nq > 4; FA_ERR_ARG for a descale that is not finite and
+ * > 0.
+ */
+int fa_fwd_splitkv_fp8kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                         const int32_t* kv_len, float k_descale, float v_descale, int num_splits,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Forward pass on 8-bit floating point inputs.  The pages name native FP8 as
  * FlashAttention-3's way to halve memory traffic (datacamp "Penjelasan Flash
  * Attention", Flash Attention 3, "Presisi FP8 native") without a format or

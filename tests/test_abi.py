@@ -189,6 +189,17 @@ def test_fp8_validation(lib):
     assert f8(N=0, q=None) == 0
 
 
+def test_fp8kv_decode_validation(lib):
+    P = FAKE
+    need = lib.fa_fwd_splitkv_workspace_bytes(1, 2, 3, 500, 128, 0)
+
+    def call(Nq=3, dk=1.0, dv=1.0, d=128, ns=0):
+        return lib.fa_fwd_splitkv_fp8kv(P, P, P, P, P, 1, 2, Nq, 500, d, 0.1, 0, None, dk, dv, ns, P, need, None)
+    assert call(Nq=5) == 2                              # decoding only: at most 4 queries
+    assert call(dk=0.0) == 7 and call(dv=float("nan")) == 7
+    assert call(d=96) == 2 and call(ns=2000) == 7
+
+
 def test_debug_visits_validation(lib):
     assert lib.fa_debug_visits(3, 1, 1, 128, 64, 0, None, None, 0, FAKE, None, 0, None) == 7
     assert lib.fa_debug_visits(0, 1, 1, 128, 64, 0, None, None, 0, None, None, 0, None) == 1

@@ -154,3 +154,72 @@ def test_splitkv_full_size_sampled(which):
     got_o = np.stack([o[b, h][rows] for b, h in heads])
     got_l = np.stack([lse[b, h][rows] for b, h in heads])
     compare_forward(got_o, got_l, O, L, "bf16", f"splitkv {which}")
+
+
+# ---------------------------------------------------------------- E4M3 key/value cache
+
+def run_fp8kv(q, k8, v8, dk, dv, scale, causal=False, kv_len=None, num_splits=0):
+    import torch
+
+    import exact_io_aware_flashattention_amd as fa
+    tq = to_dev(q, "bf16")
+    tk, tv = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (k8, v8))
+    kl = None if kv_len is None else torch.from_numpy(np.asarray(kv_len, np.int32)).cuda()
+    o, lse = fa.fa_fwd_splitkv_fp8kv(tq, tk, tv, float(dk), float(dv), scale=scale, causal=causal, kv_len=kl,
+                                     num_splits=num_splits)
+    torch.cuda.synchronize()
+    return host(o), lse.cpu().numpy().astype(np.float64)
+
+
+FP8KV_CASES = [
+    # B, H, Nq, Nk, d, causal, kv, num_splits
+    (4, 8, 1, 5000, 128, False, False, 0),
+    (3, 4, 3, 2500, 64, True, True, 0),
+    (2, 2, 2, 3001, 256, True, False, 7),
+    (1, 2, 4, 5, 128, True, False, 0),
+]
+
+
+@pytest.mark.parametrize("case", FP8KV_CASES, ids=lambda c: "B{}H{}q{}k{}d{}{}{}s{}".format(
+    c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "", "p" if c[6] else "", c[7]))
+def test_fp8kv_decode_parity(case):
+    """Decoding against an E4M3 K/V cache: the oracle is exact attention of the
+    bf16 queries against the real values of the codes; every product is exact
+    and the probabilities stay fp32, so the bf16 bounds apply."""
+    from oracle import fp8 as ofp8
+    from workloads import quantize_e4m3
+    B, H, Nq, Nk, d, causal, kv, ns = case
+    q, k, v = draw(B, H, Nq, Nk, d, 700 + Nq + Nk)
+    (k8, dk), (v8, dv) = quantize_e4m3(k), quantize_e4m3(v)
+    kv_len = None
+    if kv:
+        kv_len = draw_kv_len(B, 0, Nk, 710 + Nk)
+        kv_len[0] = 0
+    say(f"fp8kv decode {case}")
+    scale = 1 / np.sqrt(d)
+    o, lse = run_fp8kv(q, k8, v8, dk, dv, scale, causal, kv_len, ns)
+    K, V = ofp8.dequantize(k8, dk), ofp8.dequantize(v8, dv)
+    O, L = oracle(q, K, V, scale, causal, kv_len)
+    compare_forward(o.reshape(B * H, Nq, d), lse.reshape(B * H, Nq), O, L, "bf16", f"fp8kv {case}")
+
+
+def test_fp8kv_decode_full_size_sampled():
+    """The decode benchmark shape (B16 H16, one query against 16384 keys) with
+    the cache quantized per tensor, as bench.py --splitkv decode --fp8 times
+    it, on sampled heads."""
+    from oracle import fp8 as ofp8
+    from workloads import quantize_e4m3
+    w = SPLITKV_WORKLOADS["decode"]
+    B, H, Nq, Nk, d = w["B"], w["H"], w["Nq"], w["Nk"], w["d"]
+    q, k, v = draw_split_qkv(B, H, Nq, Nk, d, w["sigma"], w["seed"])
+    (k8, dk), (v8, dv) = quantize_e4m3(k), quantize_e4m3(v)
+    say("fp8kv decode full size")
+    o, lse = run_fp8kv(q, k8, v8, dk, dv, 1 / np.sqrt(d))
+    rng = np.random.Generator(np.random.PCG64(720))
+    heads = [(int(x) // H, int(x) % H) for x in np.unique(np.r_[0, B * H - 1, rng.integers(0, B * H, 8)])]
+    K = {bh: ofp8.dequantize(k8[bh], dk) for bh in heads}
+    V = {bh: ofp8.dequantize(v8[bh], dv) for bh in heads}
+    O = np.stack([attention.head_forward(q[b, h], K[(b, h)], V[(b, h)], 1 / np.sqrt(d))[0] for b, h in heads])
+    L = np.stack([attention.head_forward(q[b, h], K[(b, h)], V[(b, h)], 1 / np.sqrt(d))[1] for b, h in heads])
+    compare_forward(np.stack([o[b, h] for b, h in heads]), np.stack([lse[b, h] for b, h in heads]), O, L, "bf16",
+                    "fp8kv decode full")
