@@ -184,3 +184,24 @@ def test_dropout_full_size_sampled():
                         f"dropout full h{h}")
         dQ = odrop.head_backward_rows(Q, K, V, dO, w.scale, h, t, seed, rows, causal=True)
         compare_grad(out["dq"][0, h][rows], dQ, "bf16", f"dropout full h{h} dq rows")
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_dropout_split_key_column(d):
+    """Dropout with a block mask whose key columns are split over work-groups
+    in dK/dV (chunk 16 cells, set columns visited by 40 query cells): the
+    split partial sums and, at d = 256, both dK/dV passes with their own plans."""
+    from test_parity import split_mask
+    N = 40 * 128 - 37
+    T = -(-N // 128)
+    bm = split_mask(T, 390 + d, 20)
+    B, H, t, seed = 1, 1, 51, 0x5151 + d
+    q, k, v, do = draw_qkvdo(B, H, N, d, "bf16", 1.0, 391 + d)
+    say(f"dropout split column d={d} N={N}")
+    out = run(q, k, v, do, 1 / np.sqrt(d), t, seed, block_mask=bm)
+    O, lse = odrop.forward(q, k, v, 1 / np.sqrt(d), t, seed, block_mask=bm)
+    keep_frac = 1 - t / 256
+    compare_forward(out["o"] * keep_frac, out["lse"], O * keep_frac, lse, "bf16", f"dropout split d{d}")
+    g = odrop.backward(q, k, v, do, 1 / np.sqrt(d), t, seed, block_mask=bm)
+    for name, a, r in zip(("dq", "dk", "dv"), (out["dq"], out["dk"], out["dv"]), g):
+        compare_grad(a, r, "bf16", f"dropout split d{d} {name}")
