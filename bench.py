@@ -464,7 +464,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=4, choices=(1, 2, 3, 4, 5, 6),
+    ap.add_argument("--workload", type=int, default=4, choices=(1, 2, 3, 4, 5, 6, 7, 8),
                     help="workload to time (default 4, the long-context line)")
     ap.add_argument("--sweep", action="store_true", help="time the N = 1K..16K sweep (one JSON line per shape)")
     ap.add_argument("--dropout", type=float, default=0.0,
@@ -556,6 +556,8 @@ def main():
             3: "BERT-large shaped: B=32 H=16 N=512 d=64 bf16, key padding kv_len ~ U[128, 512], scale 1/8",
             4: "long-context: B=1 H=16 N=16384 d=128 bf16 causal, scale 1/sqrt(128)",
             6: "long-context, head dim 256: B=1 H=8 N=16384 d=256 bf16 causal, scale 1/16",
+            7: "long-context, head dim 96: B=1 H=16 N=16384 d=96 bf16 causal, scale 1/sqrt(96)",
+            8: "long-context, head dim 160: B=1 H=16 N=16384 d=160 bf16 causal, scale 1/sqrt(160)",
             5: "block-sparse: B=1 H=8 N=65536 d=64 bf16, 128x128 cell mask (band, 2 random cells per row, "
                "first column), scale 1/8"}[args.workload]
     config = {"workload": desc, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,

@@ -22,10 +22,21 @@ struct Shape {
 
 // Size and type checks shared by every entry point.  Sets *empty when there
 // is nothing to compute.
+// Head dimensions of the bf16 kernels; fp32 has 64 and 128.
+bool bf16_head_dim(int d) { return d == 64 || d == 96 || d == 128 || d == 160 || d == 256; }
+
+// d = 96 and 160 are staged in LDS with padded rows whose pad chunks are
+// loaded from the offset 2^31 (past the head), so a head (N rows) must span
+// at most 2^31 bytes.
+bool head_fits(long long N, int d) {
+  const bool padded = d == 96 || d == 160;
+  return N * d <= (padded ? (1LL << 30) : 0x7fffffffLL);
+}
+
 int check_shape(const Shape& s, const uint8_t* block_mask, bool* empty) {
   if (s.dtype != FA_BF16 && s.dtype != FA_F32) return FA_ERR_DTYPE;
   if (s.B < 0 || s.H < 0 || s.N < 0) return FA_ERR_SHAPE;
-  if (s.d != 64 && s.d != 128 && !(s.d == 256 && s.dtype == FA_BF16)) return FA_ERR_SHAPE;
+  if (s.dtype == FA_BF16 ? !bf16_head_dim(s.d) : (s.d != 64 && s.d != 128)) return FA_ERR_SHAPE;
   *empty = (s.B == 0 || s.H == 0 || s.N == 0);
   if (*empty) return FA_OK;
   const long long T = (s.N + kCell - 1) / kCell;
@@ -35,7 +46,7 @@ int check_shape(const Shape& s, const uint8_t* block_mask, bool* empty) {
   // preprocess at most 32 threads per row.  In-head offsets stay within int.
   if (T * s.H * s.B + fa::SPLIT_MAX_ITEMS >= (1LL << 32) / fa::NT_HOST) return FA_ERR_SHAPE;
   if ((long long)s.B * s.H * s.N >= (1LL << 32) / 32 - fa::NT_HOST) return FA_ERR_SHAPE;
-  if ((long long)s.N * s.d > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (!head_fits(s.N, s.d)) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -213,7 +224,7 @@ int pre_impl(const void* o, const void* dO, float* delta, int B, int H, int N, i
 }
 
 size_t split_bytes(int N, int d, int dtype, int has_block_mask) {
-  if (N <= 0 || (d != 64 && d != 128 && d != 256) || dtype != FA_BF16 || !has_block_mask) return 0;
+  if (N <= 0 || !bf16_head_dim(d) || dtype != FA_BF16 || !has_block_mask) return 0;
   return fa::split_ws_bytes(N, d);
 }
 
@@ -283,12 +294,12 @@ int splitkv_plan(int B, int H, int Nq, int Nk, int num_splits, KvPlan* p) {
 int check_splitkv_shape(int B, int H, int Nq, int Nk, int d, int dtype, bool* empty) {
   if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_DTYPE;
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128 && d != 256) return FA_ERR_SHAPE;
+  if (!bf16_head_dim(d)) return FA_ERR_SHAPE;
   *empty = (B == 0 || H == 0 || Nq == 0);
   if (*empty) return FA_OK;
   if (dtype != FA_BF16) return FA_ERR_DTYPE;
   if ((long long)B * H * Nq * (d / 4) >= (1LL << 32) - fa::NT_HOST) return FA_ERR_SHAPE;
-  if ((long long)Nq * d > 0x7fffffffLL || (long long)Nk * d > 0x7fffffffLL) return FA_ERR_SHAPE;
+  if (!head_fits(Nq, d) || !head_fits(Nk, d)) return FA_ERR_SHAPE;
   return FA_OK;
 }
 

@@ -10,9 +10,13 @@
 // and dO tile travels HBM -> LDS by buffer-to-LDS loads (no register staging,
 // no LDS writes by the waves), is stored once, row-major and swizzled, and is
 // read back either by rows (ds_read_b128) or transposed (ds_read_b64_tr_b16)
-// for the products that contract over the tile rows.  All three kernels run
-// two waves per SIMD (at most 256 registers per wave) so one wave's softmax
-// and mask work overlaps the other wave's matrix-core work.
+// for the products that contract over the tile rows.  Up to d = 128 all three
+// kernels run two waves per SIMD (at most 256 registers per wave) so one
+// wave's softmax and mask work overlaps the other wave's matrix-core work.
+// Head dimensions: multiples of 32 from 64 to 256 (instantiated: 64, 96, 128,
+// 160, 256); a dimension that is not a power of two uses the LDS tile layout
+// of the next power of two (fa_tile.hpp) and the loops run over its D / 16
+// contraction steps and D / 32 output blocks.
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 #include "fa_tile.hpp"
@@ -61,12 +65,12 @@ __device__ __forceinline__ void zero(f32x16& x) {
 template <int D>
 struct FwdB {
   static constexpr int BC = 64;                 // keys per tile (one DMA unit of K or V)
-  static constexpr int TILE = BC * D * 2;       // bytes of one K or V tile
+  static constexpr int TILE = BC * BTile<D>::ROWB;   // LDS bytes of one K or V tile
   static constexpr int SSTEPS = D / 16;
   static constexpr int NB = D / 32;
-  // waves per SIMD: two (<= 256 registers) up to d = 128; d = 256 needs the
-  // accumulation registers of a single wave per SIMD
-  static constexpr int OCC = D == 256 ? 1 : 2;
+  // waves per SIMD: two (<= 256 registers) up to d = 128; above, the
+  // accumulation and operand registers need a single wave per SIMD
+  static constexpr int OCC = D > 128 ? 1 : 2;
 };
 
 // Forward, software-pipelined over 32-key sub-blocks t = 0, 1, ... of the walk:
@@ -330,26 +334,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC
 
 template <int D>
 struct DkdvB {
-  static constexpr int BQ = D >= 128 ? 32 : 64;     // queries per stage
-  static constexpr int TSH = D >= 128 ? 5 : 6;
+  static constexpr int BQ = D > 64 ? 32 : 64;       // queries per stage
+  static constexpr int TSH = D > 64 ? 5 : 6;
   static constexpr int QS = BQ / 32;
-  static constexpr int TILE = BQ * D * 2;           // one Q or dO tile (bytes)
+  static constexpr int TILE = BQ * BTile<D>::ROWB;  // one Q or dO tile (LDS bytes)
   static constexpr int STAGE = 2 * TILE + 2 * BQ * 4;   // Q, dO, lse*log2e, delta
-  static constexpr int VRES = CELL * D * 2;         // V of the work-group's 128 keys
+  static constexpr int VRES = CELL * BTile<D>::ROWB;    // V of the work-group's 128 keys
   static constexpr int SSTEPS = D / 16;
   static constexpr int NB = D / 32;
-  // waves per SIMD: d = 256 holds one wave per SIMD, except the dV pass,
+  // d > 128 runs passes 1 and 2 (below)
+  static constexpr bool TWO_PASS = D > 128;
+  // waves per SIMD: d > 128 holds one wave per SIMD, except the dV pass,
   // which keeps no V tile in LDS (two work-groups fit) and needs only the dV
   // accumulators
-  static constexpr int occ(int pass) { return D == 256 && pass != 1 ? 1 : 2; }
+  static constexpr int occ(int pass) { return TWO_PASS && pass != 1 ? 1 : 2; }
 };
 
 // SPLIT (block mask present): work-groups [0, SPLIT_MAX_ITEMS) take the split
 // items of the plan (a chunk of a long column each; surplus ones exit), the
 // rest take one column each and exit if the column is split.
 // PASS: 0 accumulates dK and dV together; 1 only dV (S, P); 2 only dK (S, dP,
-// dS).  d = 256 runs passes 1 and 2: dK and dV together would need 256
-// accumulator registers per lane besides K's 64, more than one wave holds
+// dS).  d > 128 runs passes 1 and 2: at d = 256 dK and dV together would need
+// 256 accumulator registers per lane besides K's 64, more than one wave holds
 // without spilling; each pass holds half, for one more Q K^T product.
 template <int D, int MODE, bool SPLIT, int PASS = 0>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DkdvB<D>::occ(PASS), DkdvB<D>::occ(PASS)))) void
@@ -627,11 +633,11 @@ dkdv_bf16_kernel(AttnArgs a) {
 template <int D>
 struct DqB {
   static constexpr int BC = 64;
-  static constexpr int TILE = BC * D * 2;
+  static constexpr int TILE = BC * BTile<D>::ROWB;
   static constexpr int STAGE = 2 * TILE;        // K, V
   static constexpr int SSTEPS = D / 16;
   static constexpr int NB = D / 32;
-  static constexpr int OCC = D == 256 ? 1 : 2;  // waves per SIMD
+  static constexpr int OCC = D > 128 ? 1 : 2;   // waves per SIMD
 };
 
 template <int D, int MODE>
@@ -804,8 +810,8 @@ static hipError_t launch_dkdv_pass(const AttnArgs& a, bool walk_only, hipStream_
       hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_WALK, false>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  if constexpr (D == 256 && PASS == 0) {
-    return hipErrorInvalidValue;   // d = 256 computes in passes 1 and 2 only
+  if constexpr (DkdvB<D>::TWO_PASS && PASS == 0) {
+    return hipErrorInvalidValue;   // d > 128 computes in passes 1 and 2 only
   } else {
     if (a.mask) {
       if (a.drop_t)
@@ -824,7 +830,7 @@ static hipError_t launch_dkdv_pass(const AttnArgs& a, bool walk_only, hipStream_
 
 template <int D>
 static hipError_t launch_dkdv_b(const AttnArgs& a, bool walk_only, hipStream_t s) {
-  if constexpr (D == 256) {
+  if constexpr (DkdvB<D>::TWO_PASS) {
     if (walk_only) return launch_dkdv_pass<D, 0>(a, true, s);
     const hipError_t e = launch_dkdv_pass<D, 1>(a, false, s);
     if (e != hipSuccess) return e;
@@ -866,16 +872,27 @@ __global__ __launch_bounds__(NT) void splitkv_merge_kernel(AttnArgs a) {
   if (g == 0) a.lse[row] = l > 0.f ? (m + __log2f(l)) * LN2 : neg_inf();
 }
 
+// Calls F<D>() for the head dimension d (one of 64, 96, 128, 160, 256; the
+// entry points have checked it).
+template <typename F>
+static hipError_t by_head_dim(int d, F&& f) {
+  using std::integral_constant;
+  switch (d) {
+    case 64: return f(integral_constant<int, 64>());
+    case 96: return f(integral_constant<int, 96>());
+    case 160: return f(integral_constant<int, 160>());
+    case 256: return f(integral_constant<int, 256>());
+    default: return f(integral_constant<int, 128>());
+  }
+}
+
 hipError_t launch_splitkv_merge(const AttnArgs& a, int d, hipStream_t s) {
   const long long threads = (long long)a.B * a.H * a.N * (d / 4);
   const dim3 grid((unsigned)((threads + NT - 1) / NT));
-  if (d == 64)
-    hipLaunchKernelGGL((splitkv_merge_kernel<64>), grid, dim3(NT), 0, s, a);
-  else if (d == 256)
-    hipLaunchKernelGGL((splitkv_merge_kernel<256>), grid, dim3(NT), 0, s, a);
-  else
-    hipLaunchKernelGGL((splitkv_merge_kernel<128>), grid, dim3(NT), 0, s, a);
-  return hipGetLastError();
+  return by_head_dim(d, [&](auto D) {
+    hipLaunchKernelGGL((splitkv_merge_kernel<decltype(D)::value>), grid, dim3(NT), 0, s, a);
+    return hipGetLastError();
+  });
 }
 
 template <int D>
@@ -890,23 +907,17 @@ static hipError_t launch_splitkv_b(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fwd_splitkv_bf16(const AttnArgs& a, int d, hipStream_t s) {
-  return d == 64 ? launch_splitkv_b<64>(a, s) : d == 256 ? launch_splitkv_b<256>(a, s) : launch_splitkv_b<128>(a, s);
+  return by_head_dim(d, [&](auto D) { return launch_splitkv_b<decltype(D)::value>(a, s); });
 }
 
 hipError_t launch_fwd_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s) {
-  return d == 64    ? launch_fwd_b<64>(a, walk_only, s)
-         : d == 256 ? launch_fwd_b<256>(a, walk_only, s)
-                    : launch_fwd_b<128>(a, walk_only, s);
+  return by_head_dim(d, [&](auto D) { return launch_fwd_b<decltype(D)::value>(a, walk_only, s); });
 }
 hipError_t launch_dkdv_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s) {
-  return d == 64    ? launch_dkdv_b<64>(a, walk_only, s)
-         : d == 256 ? launch_dkdv_b<256>(a, walk_only, s)
-                    : launch_dkdv_b<128>(a, walk_only, s);
+  return by_head_dim(d, [&](auto D) { return launch_dkdv_b<decltype(D)::value>(a, walk_only, s); });
 }
 hipError_t launch_dq_bf16(const AttnArgs& a, int d, bool walk_only, hipStream_t s) {
-  return d == 64    ? launch_dq_b<64>(a, walk_only, s)
-         : d == 256 ? launch_dq_b<256>(a, walk_only, s)
-                    : launch_dq_b<128>(a, walk_only, s);
+  return by_head_dim(d, [&](auto D) { return launch_dq_b<decltype(D)::value>(a, walk_only, s); });
 }
 
 }  // namespace fa

@@ -23,16 +23,26 @@ namespace fa {
 
 // ---------------------------------------------------------------- preprocess
 
+// Threads per row of the delta pre-pass: one 16-byte chunk each, rounded up
+// to a power of two for the shuffle reduction (d = 96, 160: the extra
+// threads add zero).
+template <typename T, int D>
+constexpr int pre_threads_per_row() {
+  int t = 1;
+  while (t < D / ET<T>::CW) t *= 2;
+  return t;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(NT) void bwd_pre_kernel(AttnArgs a) {
   constexpr int CW = ET<T>::CW;
-  constexpr int TPR = D / CW;           // threads per row
+  constexpr int TPR = pre_threads_per_row<T, D>();   // threads per row
   constexpr int RPB = NT / TPR;         // rows per block
   const long long rows = (long long)a.B * a.H * a.N;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
   const int part = threadIdx.x % TPR;
   float acc = 0.f;
-  if (row < rows) {
+  if (row < rows && part < D / CW) {
     const T* o = reinterpret_cast<const T*>(a.o) + row * D + part * CW;
     const T* g = reinterpret_cast<const T*>(a.dO) + row * D + part * CW;
     const u32x4 ov = ld16(o), gv = ld16(g);
@@ -473,7 +483,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occ<T>::W, O
 
 template <typename T, int D>
 static hipError_t launch_pre_t(const AttnArgs& a, hipStream_t s) {
-  constexpr int RPB = NT / (D / ET<T>::CW);
+  constexpr int RPB = NT / pre_threads_per_row<T, D>();
   const long long rows = (long long)a.B * a.H * a.N;
   const long long nblk = (rows + RPB - 1) / RPB;
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)nblk), dim3(NT), 0, s, a);
@@ -501,8 +511,15 @@ static hipError_t launch_dq_t(const AttnArgs& a, bool walk_only, hipStream_t s) 
 }
 
 hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int d, hipStream_t s) {
-  if (dtype == 0)
-    return d == 64 ? launch_pre_t<bf16, 64>(a, s) : d == 256 ? launch_pre_t<bf16, 256>(a, s) : launch_pre_t<bf16, 128>(a, s);
+  if (dtype == 0) {
+    switch (d) {
+      case 64: return launch_pre_t<bf16, 64>(a, s);
+      case 96: return launch_pre_t<bf16, 96>(a, s);
+      case 160: return launch_pre_t<bf16, 160>(a, s);
+      case 256: return launch_pre_t<bf16, 256>(a, s);
+      default: return launch_pre_t<bf16, 128>(a, s);
+    }
+  }
   return d == 64 ? launch_pre_t<float, 64>(a, s) : launch_pre_t<float, 128>(a, s);
 }
 

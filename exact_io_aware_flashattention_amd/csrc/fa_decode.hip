@@ -13,9 +13,12 @@
 // (datacamp "Penjelasan Flash Attention", Flash Attention 2, "Paralelisme
 // sepanjang panjang sekuens").
 //
-// Data movement.  A key row of d bf16 is d/8 16-byte chunks; one load
-// instruction of a wave covers 64 / (d/8) whole consecutive rows (1 KB
-// contiguous), lane l taking chunk l % (d/8) of row l / (d/8).  A block is G
+// Data movement.  A key row of d bf16 is d/8 16-byte chunks, served by LPR
+// lanes (d/8 rounded up to a power of two); one load instruction of a wave
+// covers 64 / LPR whole consecutive rows (1 KB contiguous when d is a power
+// of two), lane l taking chunk l % LPR of row l / LPR.  Lanes past a row's
+// last chunk (d = 96, 160) load from past the end of the buffer, read zeros
+// and add nothing.  A block is G
 // such loads of K and G of V; the next block's loads are issued before the
 // current block is computed, so each wave keeps 2 G KB in flight and needs no
 // LDS and no barrier.  Loads go through a buffer resource whose size ends at
@@ -42,7 +45,8 @@ template <int D, bool F8>
 struct DecCfg {
   static constexpr int RB = F8 ? D : 2 * D;   // bytes per key row
   static constexpr int EPL = F8 ? 16 : 8;     // features per lane (one 16-byte chunk)
-  static constexpr int LPR = RB / 16;         // lanes per key row
+  static constexpr int CPR = RB / 16;         // chunks per key row
+  static constexpr int LPR = CPR <= 4 ? 4 : CPR <= 8 ? 8 : CPR <= 16 ? 16 : 32;   // lanes per key row
   static constexpr int KPI = 64 / LPR;        // key rows per load instruction
   static constexpr int G = 8;                 // load instructions per block and tensor
   static constexpr int KB = G * KPI;          // keys per block: 16 .. 64 (bf16), 32 .. 128 (E4M3)
@@ -123,6 +127,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(AttnArgs a) {
   const int b = bh / a.H;
   const int Nq = a.N, NK = a.Nk;
   const int r = lane / C::LPR, c = lane % C::LPR;
+  const bool pad = c >= C::CPR;   // a lane past the row's last chunk (d = 96, 160)
 
   // key j is allowed for query i iff j < lim[i]
   const int kvl = a.kv_len ? min(max(a.kv_len[b], 0), NK) : NK;
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(AttnArgs a) {
   for (int i = 0; i < NQ; ++i)
 #pragma unroll
     for (int u = 0; u < C::EPL / 8; ++u)
-      qv[i][u] = i < Nq ? ld16(Qh + (size_t)i * D + C::EPL * c + 8 * u) : u32x4{0, 0, 0, 0};
+      qv[i][u] = i < Nq && !pad ? ld16(Qh + (size_t)i * D + C::EPL * c + 8 * u) : u32x4{0, 0, 0, 0};
 
   float m_run[NQ], neg_mu[NQ], thr[NQ], l_run[NQ], acc[NQ][C::EPL];
 #pragma unroll
@@ -172,19 +177,17 @@ __global__ __launch_bounds__(NT) void decode_kernel(AttnArgs a) {
         const_cast<unsigned char*>(reinterpret_cast<const unsigned char*>(a.v) + head), (short)0, (int)bytes,
         0x00020000);
     const int voff0 = r * C::RB + 16 * c;
+    // pad lanes: an offset past the range (bytes <= PAD_OFF), read as zeros
+    auto offset = [&](int j) { return pad ? (int)PAD_OFF : voff0 + j * C::RB; };
 
     u32x4 kA[C::G], vA[C::G], kB[C::G], vB[C::G];
     auto load = [&](u32x4 (&kb)[C::G], u32x4 (&vb)[C::G], int j0) {
 #pragma unroll
-      for (int g = 0; g < C::G; ++g) {
-        const int off = voff0 + (j0 + g * C::KPI) * C::RB;
-        kb[g] = __builtin_amdgcn_raw_buffer_load_b128(rsK, off, 0, kStream);
-      }
+      for (int g = 0; g < C::G; ++g)
+        kb[g] = __builtin_amdgcn_raw_buffer_load_b128(rsK, offset(j0 + g * C::KPI), 0, kStream);
 #pragma unroll
-      for (int g = 0; g < C::G; ++g) {
-        const int off = voff0 + (j0 + g * C::KPI) * C::RB;
-        vb[g] = __builtin_amdgcn_raw_buffer_load_b128(rsV, off, 0, kStream);
-      }
+      for (int g = 0; g < C::G; ++g)
+        vb[g] = __builtin_amdgcn_raw_buffer_load_b128(rsV, offset(j0 + g * C::KPI), 0, kStream);
     };
     auto compute = [&](const u32x4 (&kb)[C::G], const u32x4 (&vb)[C::G], int j0) {
       float s[NQ][C::G];
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(AttnArgs a) {
     const float l_tot = wave_sum(c == 0 ? l_run[i] : 0.f);
     if (i < Nq) {
       const size_t prow = ((size_t)split * BH + bh) * Nq + i;
-      if (r == 0) {
+      if (r == 0 && !pad) {
         // the value descale (E4M3 V) is applied here, so the merge is shared
         const float vs = F8 ? a.v_descale : 1.f;
         float* po = a.part_o + prow * D + C::EPL * c;
@@ -300,18 +303,21 @@ hipError_t launch_decode_d(const AttnArgs& a, hipStream_t s) {
   return launch_decode<D, 4, F8>(a, s);
 }
 
+template <bool F8>
+hipError_t launch_decode_any(const AttnArgs& a, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_decode_d<64, F8>(a, s);
+    case 96: return launch_decode_d<96, F8>(a, s);
+    case 160: return launch_decode_d<160, F8>(a, s);
+    case 256: return launch_decode_d<256, F8>(a, s);
+    default: return launch_decode_d<128, F8>(a, s);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_fwd_decode_bf16(const AttnArgs& a, int d, hipStream_t s) {
-  return d == 64    ? launch_decode_d<64, false>(a, s)
-         : d == 256 ? launch_decode_d<256, false>(a, s)
-                    : launch_decode_d<128, false>(a, s);
-}
+hipError_t launch_fwd_decode_bf16(const AttnArgs& a, int d, hipStream_t s) { return launch_decode_any<false>(a, d, s); }
 
-hipError_t launch_fwd_decode_e4m3kv(const AttnArgs& a, int d, hipStream_t s) {
-  return d == 64    ? launch_decode_d<64, true>(a, s)
-         : d == 256 ? launch_decode_d<256, true>(a, s)
-                    : launch_decode_d<128, true>(a, s);
-}
+hipError_t launch_fwd_decode_e4m3kv(const AttnArgs& a, int d, hipStream_t s) { return launch_decode_any<true>(a, d, s); }
 
 }  // namespace fa

@@ -1,8 +1,9 @@
 // bf16 tiles staged in LDS by direct buffer-to-LDS loads, and the two ways the
 // matrix-core operands are read back from them (gfx950).
 //
-// Layout: a tile of R rows x D bf16 columns is stored row-major (D * 2 bytes
-// per row) with its 16-byte chunks XOR-swizzled per row: logical chunk c of
+// Layout: a tile of R rows x D bf16 columns is stored row-major (ROWB bytes
+// per row, D * 2 when D is a power of two) with its 16-byte chunks
+// XOR-swizzled per row: logical chunk c of
 // row r sits at physical chunk c ^ swz(r).  The LDS has 64 four-byte banks
 // (256 bytes per bank line), so a 256-byte row covers every bank once and a
 // 128-byte row half of them.  The two read kinds and what they need:
@@ -18,11 +19,20 @@
 // XOR with swz(r) < 16 changes only those four bits, so the d = 128 swizzle
 // serves d = 256 unchanged.
 //
+// Head dimensions that are not a power of two (96, 160) keep the LDS layout of
+// the next power of two (128, 256): each LDS row has room for DL columns, of
+// which the first D hold the row and the rest are never read.  The swizzles,
+// bank analysis and transposed reads are then those of d = DL; only the global
+// rows are D * 2 bytes apart.
+//
 // Loads: buffer_load_dwordx4 with the LDS-destination form writes 64 lanes x
 // 16 bytes contiguously at the LDS address in M0, so lane t of a load
 // instruction fetches the global chunk that belongs at physical position t.
 // The buffer resource spans exactly the valid rows of the head, so rows at or
-// beyond N read as zeros without any per-lane branch.  The load is issued by
+// beyond N read as zeros without any per-lane branch.  Lanes whose LDS
+// position holds a pad chunk (logical chunk >= D / 8) get the offset PAD_OFF,
+// past the end of every head's range, so they write zeros and read no memory;
+// this needs every head to span at most PAD_OFF bytes.  The load is issued by
 // inline assembly: when the compiler sees an LDS-destination load it cannot
 // tell which LDS bytes it writes, and waits for it (vmcnt(0)) before every
 // later LDS read -- including the reads of the tile being computed, which
@@ -38,13 +48,18 @@ namespace fa {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+constexpr uint32_t PAD_OFF = 0x80000000u;
+
 template <int D>
 struct BTile {
-  static constexpr int ROWB = D * 2;          // bytes per row
-  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static_assert(D % 32 == 0 && D >= 64 && D <= 256, "head dimension: a multiple of 32 in [64, 256]");
+  static constexpr int DL = D <= 64 ? 64 : D <= 128 ? 128 : 256;   // columns an LDS row has room for
+  static constexpr int ROWB = DL * 2;         // LDS bytes per row
+  static constexpr int CPR = DL / 8;          // 16-byte chunk positions per LDS row
+  static constexpr int VC = D / 8;            // chunks that hold data (the rest is padding)
   static constexpr int ROWS_PER_LOAD = 1024 / ROWB;   // rows one wave-wide load fills
   __host__ __device__ static constexpr int swz(int r) {
-    return D >= 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    return DL >= 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
   }
   __device__ static __forceinline__ int off(int r, int c) { return r * ROWB + ((c ^ swz(r)) << 4); }
 };
@@ -59,7 +74,7 @@ __device__ __forceinline__ u32x4 rows_rsrc(const void* head, int N, int D, int r
   const uint64_t p = reinterpret_cast<uint64_t>(head) + (uint64_t)(uint32_t)row0 * (uint32_t)(D * 2);
   return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p),
                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu),
-               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(max(N - row0, 0) * D * 2)), 0x00020000u};
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)max(N - row0, 0) * (uint32_t)(D * 2)), 0x00020000u};
 }
 
 // One wave-wide 16-byte-per-lane load into LDS at lds (+ 16 * lane).
@@ -73,10 +88,10 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, unsigned char* lds, int voff) 
 
 // Loads of an R-row tile spread over the NW waves of the work-group: wave w
 // issues the wave-wide loads i = j * NW + w (j < NJ), load i filling rows
-// [i * RPL, (i + 1) * RPL) (RPL rows per 1024 bytes).  When the swizzle
-// repeats every NW * RPL rows (d = 64, 128) the logical chunk a lane fetches
-// is the same for every j and the lane's byte offset inside the tile is
-// voff[0] + j * NW * 1024; otherwise (d = 256, two rows per load) the offsets
+// [i * RPL, (i + 1) * RPL) (RPL rows per 1024 LDS bytes).  When the swizzle
+// repeats every NW * RPL rows (d <= 128) the logical chunk a lane fetches
+// is the same for every j and the lane's byte offset inside the head is
+// voff[0] + j * NW * RPL * D * 2; otherwise (d > 128, two rows per load) the offsets
 // of one swizzle period are kept and each later period gets its own buffer
 // resource based at its first row (the range check of a buffer load covers the
 // per-lane offset, so rows past N still read as zeros).  Either way the
@@ -92,8 +107,8 @@ __host__ __device__ constexpr bool swizzle_repeats(int nj) {
   return true;
 }
 
-// Smallest k such that the swizzle repeats every k * NW loads (1 for d = 64
-// and 128; 2 for d = 256, whose 16-row swizzle period spans 8 two-row loads).
+// Smallest k such that the swizzle repeats every k * NW loads (1 for d <= 128;
+// 2 for d > 128, whose 16-row swizzle period spans 8 two-row loads).
 template <int D, int NW>
 __host__ __device__ constexpr int swizzle_period_loads() {
   for (int k = 1; k < 16; ++k) {
@@ -124,18 +139,19 @@ struct TileDma {
       const int c = (lane % TL::CPR) ^ TL::swz(lr);               // logical chunk at position lane
       const int off0 = (lr * D + c * 8) * 2;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) voff[j] = off0 + j * NW * 1024;
+      for (int j = 0; j < NJ; ++j)
+        voff[j] = c < TL::VC ? off0 + j * NW * TL::ROWS_PER_LOAD * D * 2 : (int)PAD_OFF;
     } else {
 #pragma unroll
       for (int j = 0; j < KP; ++j) {
         const int lr = (j * NW + wave) * TL::ROWS_PER_LOAD + lane / TL::CPR;
         const int c = (lane % TL::CPR) ^ TL::swz(lr);
-        voff[j] = (lr * D + c * 8) * 2;
+        voff[j] = c < TL::VC ? (lr * D + c * 8) * 2 : (int)PAD_OFF;
       }
     }
   }
   // Issue the loads of rows [row0, row0 + R) of head (N rows) into lds
-  // (R * D * 2 bytes); rows at or past N read as zeros.  Completion:
+  // (R * BTile<D>::ROWB bytes); rows at or past N read as zeros.  Completion:
   // s_waitcnt vmcnt(0) in every wave, then a barrier.
   __device__ __forceinline__ void load(const void* head, int N, int row0, unsigned char* lds) const {
     const int wave = wave_id();

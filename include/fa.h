@@ -25,12 +25,15 @@
  *   dtype      FA_BF16 (bf16 storage, bf16 matrix-core products, float32
  *              accumulation and softmax) or FA_F32 (float32 throughout; no
  *              step goes through a narrower type).
- *   d          64 or 128; also 256 with FA_BF16 (the head dimension FA2
- *              extends to, datacamp "Penjelasan Flash Attention", Flash
- *              Attention 2, "Dukungan untuk dimensi head yang lebih besar").  At d = 256 a work-group's tiles fill the LDS and
- *              its accumulators a whole wave's registers, so one wave runs per
- *              SIMD, and dK/dV are accumulated in two passes over the queries
- *              (dV, then dK), which costs one more Q K^T product.
+ *   d          64 or 128; with FA_BF16 also 96, 160 and 256 (FA2 extends
+ *              the head dimension up to 256, datacamp "Penjelasan Flash
+ *              Attention", Flash Attention 2, "Dukungan untuk dimensi head
+ *              yang lebih besar").  Above d = 128 a work-group's tiles fill
+ *              the LDS and its accumulators a whole wave's registers, so one
+ *              wave runs per SIMD, and dK/dV are accumulated in two passes
+ *              over the queries (dV, then dK), which costs one more Q K^T
+ *              product.  d = 96 and 160 are staged in LDS as rows of 128 and
+ *              256 columns, and need N * d <= 2^30 (else FA_ERR_SHAPE).
  *   scale      finite and > 0 (the pages write S = QK^T, i.e. scale = 1).
  *   causal     nonzero: key j is allowed for query i only if j <= i (queries
  *              and keys share positions, top-left aligned).
@@ -69,7 +72,7 @@ enum fa_dtype { FA_BF16 = 0, FA_F32 = 1 };
 enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL */
-  FA_ERR_SHAPE = 2,     /* negative size, d not 64/128 (or 256 in bf16), T > 2048 or too large */
+  FA_ERR_SHAPE = 2,     /* negative size, d not 64/128 (or 96/160/256 in bf16), T > 2048 or too large */
   FA_ERR_DTYPE = 3,     /* dtype not FA_BF16 / FA_F32 */
   FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE = 5, /* workspace smaller than the matching *_workspace_bytes() */
@@ -105,7 +108,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype, int has_blo
  * cells visit are split over several work-groups, which need a plan, arrival
  * counters and float32 partial sums for at most 1024 column chunks
  * (1024 * 2 * 128 * d * 4 bytes plus about ceil(N/128)^2 / 16 bytes; 64 MiB
- * at d = 64, 128 MiB at d = 128, 256 MiB at d = 256).  Independent of B and H.
+ * at d = 64, 128 MiB at d = 128, 256 MiB at d = 256; d / 64 * 64 MiB in
+ * general).  Independent of B and H.
  */
 size_t fa_bwd_dkdv_workspace_bytes(int N, int d, int dtype, int has_block_mask);
 
@@ -217,6 +221,8 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
  * otherwise one work-group handles a range for 128 queries of one (b, h)
  * (the matrix-core forward kernel, ranges of whole 128-key cells).
  *   q, o     [B,H,Nq,d] bf16;  k, v  [B,H,Nk,d] bf16;  lse [B,H,Nq] float32.
+ *   d        64, 96, 128, 160 or 256 (with 96 and 160, Nq * d and Nk * d
+ *            <= 2^30).
  *   causal   nonzero: queries are the last Nq of Nk positions, so key j is
  *            allowed for query i iff j <= i + Nk - Nq (for Nk = Nq this is
  *            fa_fwd's mask; queries with i + Nk - Nq < 0 have no key).

@@ -76,9 +76,17 @@ def fwd(lib, **kw):
 def test_forward_validation(lib):
     assert fwd(lib, q=None) == 1                       # FA_ERR_NULL
     assert fwd(lib, lse=None) == 1
-    assert fwd(lib, d=96) == 2                         # FA_ERR_SHAPE
-    assert fwd(lib, d=256, dtype=1) == 2               # d = 256 is bf16 only
-    assert fwd(lib, d=256, scale=-1.0) == 7            # d = 256 bf16 passes the shape check
+    for d in (32, 80, 192, 320):
+        assert fwd(lib, d=d) == 2                      # FA_ERR_SHAPE
+    for d in (96, 160, 256):
+        assert fwd(lib, d=d, dtype=1) == 2             # bf16 only
+        assert fwd(lib, d=d, scale=-1.0) == 7          # bf16 passes the shape check
+    # d = 96, 160: padded LDS rows need a head of at most 2^31 bytes (N d <= 2^30)
+    n_max = (1 << 30) // 96
+    assert fwd(lib, d=96, N=n_max, scale=-1.0) == 7
+    assert fwd(lib, d=96, N=n_max + 1, scale=-1.0) == 2
+    assert fwd(lib, d=128, N=n_max + 1, scale=-1.0) == 7
+    assert fwd(lib, d=160, N=(1 << 30) // 160 + 1, scale=-1.0) == 2
     assert fwd(lib, N=-1) == 2
     assert fwd(lib, dtype=7) == 3                      # FA_ERR_DTYPE
     assert fwd(lib, k=FAKE + 8) == 4                   # FA_ERR_ALIGN
@@ -167,7 +175,9 @@ def test_splitkv_plan_and_validation(lib):
     def call(ws=P, nbytes=need, dtype=0, ns=0, d=128, scale=0.1, Nk=500, k=P):
         return lib.fa_fwd_splitkv(P, k, P, P, P, 1, 2, 10, Nk, d, scale, 1, None, dtype, ns, ws, nbytes, None)
     assert call(dtype=1) == 3                         # bf16 only
-    assert call(d=96) == 2
+    assert call(d=80) == 2
+    assert call(d=96, scale=0.0) == 7 and call(d=160, scale=0.0) == 7   # shapes accepted
+    assert call(d=96, Nk=(1 << 30) // 96 + 1) == 2
     assert call(ns=1025) == 7 and call(ns=-1) == 7
     assert call(scale=0.0) == 7
     assert call(ws=None) == 1
@@ -197,7 +207,8 @@ def test_fp8kv_decode_validation(lib):
         return lib.fa_fwd_splitkv_fp8kv(P, P, P, P, P, 1, 2, Nq, 500, d, 0.1, 0, None, dk, dv, ns, P, need, None)
     assert call(Nq=5) == 2                              # decoding only: at most 4 queries
     assert call(dk=0.0) == 7 and call(dv=float("nan")) == 7
-    assert call(d=96) == 2 and call(ns=2000) == 7
+    assert call(d=80) == 2 and call(ns=2000) == 7
+    assert call(d=160, dk=0.0) == 7                     # d = 160 passes the shape check
 
 
 def test_debug_visits_validation(lib):

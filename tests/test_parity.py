@@ -256,9 +256,9 @@ def test_sweep_shapes_sampled_heads(shape):
     _check_heads_dense(inp, out, _sample_heads(B, 16, 3, N + d), f"sweep N{N}d{d}")
 
 
-@pytest.mark.parametrize("key", [4, 5, 6])
+@pytest.mark.parametrize("key", [4, 5, 6, 7, 8])
 def test_workload_long_sequence_sampled(key):
-    """N = 16K causal (d = 128 and 256) and N = 64K block-sparse: sampled rows of
+    """N = 16K causal (d = 96, 128, 160 and 256) and N = 64K block-sparse: sampled rows of
     O, lse and dQ and sampled key columns of dK, dV on two heads, against the
     gathered oracle."""
     inp = make_inputs(WORKLOADS[key])

@@ -48,6 +48,9 @@ CASES = [
     # head dimension 256 (dK/dV computes in two passes; the walk is shared)
     (2, 2, 600, 256, True, "bern", "rand"),
     (1, 2, 5083, 256, False, "split", None),
+    # head dimensions 96 and 160 (padded LDS rows; 160 computes dK/dV in two passes)
+    (2, 2, 600, 96, True, "bern", "rand"),
+    (1, 2, 5083, 160, False, "split", None),
 ]
 
 
@@ -69,7 +72,7 @@ def test_walk_matches_expected(case):
     run_walks(B, H, N, d, causal, bm, kv)
 
 
-@pytest.mark.parametrize("key", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("key", [2, 3, 4, 5, 6, 7, 8])
 def test_walk_workloads(key):
     w = WORKLOADS[key]
     from workloads import make_inputs

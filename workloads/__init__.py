@@ -67,6 +67,10 @@ WORKLOADS = {
     # head dimension 256 (the FA2 extension): the long-context shape with the
     # same H * d and flops as workload 4
     6: Workload(6, "long-context-d256", 1, 8, 16384, 256, "bf16", True, 1.0 / 16.0, math.sqrt(0.5)),
+    # head dimensions 96 and 160 (not powers of two): the long-context shape
+    # with d changed
+    7: Workload(7, "long-context-d96", 1, 16, 16384, 96, "bf16", True, 1.0 / math.sqrt(96.0), math.sqrt(0.5)),
+    8: Workload(8, "long-context-d160", 1, 16, 16384, 160, "bf16", True, 1.0 / math.sqrt(160.0), math.sqrt(0.5)),
 }
 
 
