@@ -11,8 +11,9 @@
 // no LDS writes by the waves), is stored once, row-major and swizzled, and is
 // read back either by rows (ds_read_b128) or transposed (ds_read_b64_tr_b16)
 // for the products that contract over the tile rows.  Up to d = 128 all three
-// kernels run two waves per SIMD (at most 256 registers per wave) so one
-// wave's softmax and mask work overlaps the other wave's matrix-core work.
+// kernels run at least two waves per SIMD (at most 256 registers per wave) so
+// one wave's softmax and mask work overlaps another wave's matrix-core work;
+// dQ at d = 64 runs three.
 // Head dimensions: multiples of 32 from 64 to 256 (instantiated: 64, 96, 128,
 // 160, 256); a dimension that is not a power of two uses the LDS tile layout
 // of the next power of two (fa_tile.hpp) and the loops run over its D / 16
@@ -454,7 +455,21 @@ dkdv_bf16_kernel(AttnArgs a) {
       issue(0);
     }
 
-    for (int it = 0; it < walk.ntiles; ++it) {
+    // The leading tiles of the walk may hold masked entries for some wave
+    // (the diagonal cell under a causal mask; every tile when the work-group's
+    // keys straddle kv_len).  Below d = 128 they run the masked body and the
+    // rest a body with no mask code, one basic block from the first product to
+    // the last (1-2 % faster at d = 64 and 96).  At d = 128 every tile takes
+    // the masked body: the mask-free body measured 1.5-3 % slower there.
+    constexpr bool PLAIN_LOOP = D < 128;
+    int n_edge = 0;
+    if (!PLAIN_LOOP || kj * CELL + CELL > kvl)
+      n_edge = walk.ntiles;
+    else if (a.causal)
+      while (n_edge < walk.ntiles && walk.tile_start(n_edge) < kj * CELL + CELL - 1) ++n_edge;
+
+    auto tile = [&](int it, auto plain_c) {
+      constexpr bool PLAIN = decltype(plain_c)::value && !DROP;
       wait_loads();
       unsigned char* st = smem + VRES + (it & 1) * C::STAGE;
       float* stats = reinterpret_cast<float*>(st + 2 * C::TILE);
@@ -473,7 +488,49 @@ dkdv_bf16_kernel(AttnArgs a) {
       const int q0 = walk.tile_start(it);
       const unsigned char* Qs = st;
       const unsigned char* dOs = st + C::TILE;
-      if (!wave_has_keys || (a.causal && kw0 > q0 + C::BQ - 1)) continue;
+      if constexpr (PLAIN) {
+#pragma unroll
+        for (int qs = 0; qs < C::QS; ++qs) {
+          f32x16 s, dp;
+          zero(s);
+          zero(dp);
+#pragma unroll
+          for (int k = 0; k < C::SSTEPS; ++k) {
+            mma(s, as_bf16x8(row_chunk<D>(Qs, 32 * qs + l32, 2 * k + h)), as_bf16x8(kf[k]));
+            if constexpr (DO_DK)
+              mma(dp, as_bf16x8(row_chunk<D>(dOs, 32 * qs + l32, 2 * k + h)),
+                  as_bf16x8(VREG ? vfr[k] : row_chunk<D>(Vs, wave * 32 + l32, 2 * k + h)));
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(stats + 32 * qs + 8 * g + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[4 * g + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], a.c, -l4[e]));
+          }
+          if constexpr (DO_DV) {
+            const PackedB pb = pack_bf16(s);
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+              for (int mm = 0; mm < 2; ++mm) mma(dv[nb], tr_operand<D>(dOs, 32 * qs + 16 * mm, 32 * nb), pb.p[mm]);
+          }
+          if constexpr (DO_DK) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 d4 = *reinterpret_cast<const f32x4*>(stats + C::BQ + 32 * qs + 8 * g + 4 * h);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) dp[4 * g + e] = s[4 * g + e] * (dp[4 * g + e] - d4[e]);
+            }
+            const PackedB db = pack_bf16(dp);
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+              for (int mm = 0; mm < 2; ++mm) mma(dk[nb], tr_operand<D>(Qs, 32 * qs + 16 * mm, 32 * nb), db.p[mm]);
+          }
+        }
+        return;
+      }
+      if (!wave_has_keys || (a.causal && kw0 > q0 + C::BQ - 1)) return;
       const bool edge = (kw0 + 32 > kvl) || (a.causal && kw0 + 31 > q0);
 #pragma unroll
       for (int qs = 0; qs < C::QS; ++qs) {
@@ -551,7 +608,11 @@ dkdv_bf16_kernel(AttnArgs a) {
             for (int mm = 0; mm < 2; ++mm) mma(dk[nb], tr_operand<D>(Qs, 32 * qs + 16 * mm, 32 * nb), db.p[mm]);
         }
       }
-    }
+    };
+    int it = 0;
+    for (; it < n_edge; ++it) tile(it, std::false_type());
+    if constexpr (PLAIN_LOOP)
+      for (; it < walk.ntiles; ++it) tile(it, std::true_type());
 
     if constexpr (SPLIT) {
       if (split_item) {
@@ -637,7 +698,10 @@ struct DqB {
   static constexpr int STAGE = 2 * TILE;        // K, V
   static constexpr int SSTEPS = D / 16;
   static constexpr int NB = D / 32;
-  static constexpr int OCC = D > 128 ? 1 : 2;   // waves per SIMD
+  // waves per SIMD: three at d = 64 (the kernel fits in 168 registers
+  // without spilling; 8-13 % faster than two on d = 64 shapes), two up to
+  // d = 128, one above
+  static constexpr int OCC = D == 64 ? 3 : D > 128 ? 1 : 2;
 };
 
 template <int D, int MODE>
@@ -705,14 +769,52 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DqB<D>::OCC,
     };
     if (walk.ntiles > 0) issue(0);
 
-    for (int it = 0; it < walk.ntiles; ++it) {
+    // The trailing tiles of the walk may hold masked entries for some wave
+    // (the diagonal cell under a causal mask, the tile that straddles
+    // kv_len).  Below d = 128 the tiles before them run a body with no mask
+    // code, one basic block over both 32-key halves, so that each half's
+    // exponentials and dS work can overlap products of the other half (dQ
+    // 3-5 % faster at d = 64).  At d = 128 every tile takes the masked body,
+    // which measured slightly faster there.
+    constexpr bool PLAIN_LOOP = D < 128;
+    int n_plain = PLAIN_LOOP ? walk.ntiles : 0;
+    while (n_plain > 0 && (walk.tile_start(n_plain - 1) + C::BC > kvl ||
+                           (a.causal && walk.tile_start(n_plain - 1) + C::BC - 1 > q_lo)))
+      --n_plain;
+
+    auto tile = [&](int it, auto plain_c) {
+      constexpr bool PLAIN = decltype(plain_c)::value && !DROP;
       wait_loads();
       __syncthreads();
       if (it + 1 < walk.ntiles) issue(it + 1);
       const int kb0 = walk.tile_start(it);
       const unsigned char* Ks = smem + (it & 1) * C::STAGE;
       const unsigned char* Vs = Ks + C::TILE;
-      if (!wave_has_rows || (a.causal && kb0 > qw0 + 31)) continue;
+      if (!wave_has_rows) return;
+      if constexpr (PLAIN) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          f32x16 s, dp;
+          zero(s);
+          zero(dp);
+#pragma unroll
+          for (int k = 0; k < C::SSTEPS; ++k) {
+            mma(s, as_bf16x8(row_chunk<D>(Ks, 32 * sb + l32, 2 * k + h)), as_bf16x8(qf[k]));
+            mma(dp, as_bf16x8(row_chunk<D>(Vs, 32 * sb + l32, 2 * k + h)), as_bf16x8(gf[k]));
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -lse2));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - del);
+          const PackedB db = pack_bf16(dp);
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) mma(dq[nb], tr_operand<D>(Ks, 32 * sb + 16 * mm, 32 * nb), db.p[mm]);
+        }
+        return;
+      }
+      if (a.causal && kb0 > qw0 + 31) return;
       const bool edge = (kb0 + C::BC > kvl) || (a.causal && kb0 + C::BC - 1 > qw0);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
@@ -756,7 +858,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DqB<D>::OCC,
 #pragma unroll
           for (int mm = 0; mm < 2; ++mm) mma(dq[nb], tr_operand<D>(Ks, 32 * sb + 16 * mm, 32 * nb), db.p[mm]);
       }
-    }
+    };
+    int it = 0;
+    if constexpr (PLAIN_LOOP)
+      for (; it < n_plain; ++it) tile(it, std::true_type());
+    for (; it < walk.ntiles; ++it) tile(it, std::false_type());
 
     if (myq < N) {
       bf16* p = reinterpret_cast<bf16*>(a.out0) + head + (size_t)myq * D;
