@@ -27,6 +27,7 @@ arithmetic intensity (compulsory bytes) against the ridge point.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -41,6 +42,19 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
 PEAK_F32_TFLOPS = 157.3        # fp32 matrix peak
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 matrix peak
+
+
+def _gc_pause():
+    """Collect now and keep Python's cyclic collector off while the timed launches
+    are enqueued: a full collection (tens of ms with torch loaded) can stall the
+    launching thread long enough for the GPU queue to drain, and the idle time
+    would be counted in whichever kernel's event interval was open."""
+    gc.collect()
+    gc.disable()
+
+
+def _gc_resume():
+    gc.enable()
 
 
 def flops_fwd(B, H, N, d, causal, cell_frac=1.0):
@@ -113,11 +127,13 @@ def run_gpu_bench_dropout(w, steps, warmup, inp, p, seed=2024):
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    _gc_pause()
     start.record(stream)
     for i in range(steps):
         step(evs[i])
     end.record(stream)
     torch.cuda.synchronize()
+    _gc_resume()
     per = {"fwd": sum(e[0].elapsed_time(e[1]) for e in evs) / steps,
            "bwd": sum(e[1].elapsed_time(e[2]) for e in evs) / steps}
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(dq).all())
@@ -168,11 +184,13 @@ def run_gpu_bench(w, steps, warmup, inp):
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    _gc_pause()
     start.record(stream)
     for i in range(steps):
         step(evs[i])
     end.record(stream)
     torch.cuda.synchronize()
+    _gc_resume()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     names = ["fwd", "pre", "dkdv", "dq"]
@@ -239,6 +257,7 @@ def run_gpu_bench_splitkv(which, steps, warmup, fp8kv=False):
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    _gc_pause()
     start.record(stream)
     for a, b in evs:
         a.record(stream)
@@ -246,6 +265,7 @@ def run_gpu_bench_splitkv(which, steps, warmup, fp8kv=False):
         b.record(stream)
     end.record(stream)
     torch.cuda.synchronize()
+    _gc_resume()
     assert bool(torch.isfinite(o).all())
     call_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
     flops, nbytes = splitkv_alg(w, fp8kv)
@@ -301,6 +321,7 @@ def run_gpu_bench_fp8(w, steps, warmup, inp):
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    _gc_pause()
     start.record(stream)
     for a, b in evs:
         a.record(stream)
@@ -308,6 +329,7 @@ def run_gpu_bench_fp8(w, steps, warmup, inp):
         b.record(stream)
     end.record(stream)
     torch.cuda.synchronize()
+    _gc_resume()
     assert bool(torch.isfinite(o.float()).all())
     call_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
     return start.elapsed_time(end) / steps, call_ms, (B, H, N, d)
