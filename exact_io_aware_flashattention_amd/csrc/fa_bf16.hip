@@ -458,11 +458,14 @@ dkdv_bf16_kernel(AttnArgs a) {
 
     // The leading tiles of the walk may hold masked entries for some wave
     // (the diagonal cell under a causal mask; every tile when the work-group's
-    // keys straddle kv_len).  Below d = 128 they run the masked body and the
+    // keys straddle kv_len).  Up to d = 128 they run the masked body and the
     // rest a body with no mask code, one basic block from the first product to
-    // the last (1-2 % faster at d = 64 and 96).  At d = 128 every tile takes
-    // the masked body: the mask-free body measured 1.5-3 % slower there.
-    constexpr bool PLAIN_LOOP = D < 128;
+    // the last, walked in pairs of tiles with compile-time LDS stages (1-7 %
+    // faster at d = 64 to 128 than one masked loop).  At d = 128 the dropout
+    // and block-mask instances keep one masked loop (the split form spills
+    // there, and measured 1 % slower with dropout); above d = 128 every tile
+    // takes the masked body.
+    constexpr bool PLAIN_LOOP = D < 128 || (D == 128 && !DROP && !SPLIT);
     int n_edge = 0;
     if (!PLAIN_LOOP || kj * CELL + CELL > kvl)
       n_edge = walk.ntiles;
@@ -618,8 +621,7 @@ dkdv_bf16_kernel(AttnArgs a) {
     if constexpr (PLAIN_LOOP) {
       for (; it < n_edge; ++it) tile(it, std::false_type(), RT());
       // the mask-free tiles with the LDS stage a compile-time constant, so
-      // every LDS address is a per-lane base plus an immediate (dK/dV 3-7 %
-      // faster at d = 64 and 96)
+      // every LDS address is a per-lane base plus an immediate
       if ((it & 1) && it < walk.ntiles) tile(it++, std::true_type(), S1());
       for (; it + 1 < walk.ntiles; it += 2) {
         tile(it, std::true_type(), S0());
@@ -629,7 +631,7 @@ dkdv_bf16_kernel(AttnArgs a) {
     } else if constexpr (D > 128) {
       // pairs of tiles with the LDS stage a compile-time constant, so every
       // LDS address is a per-lane base plus an immediate (dK/dV 20 % faster at
-      // d = 256, 28 % at d = 160; at d = 128, 4 % slower, so not used there)
+      // d = 256, 28 % at d = 160)
       for (; it < walk.ntiles; it += 2) {
         tile(it, std::false_type(), S0());
         if (it + 1 < walk.ntiles) tile(it + 1, std::false_type(), S1());
