@@ -38,6 +38,8 @@
 #include "fa_tile.hpp"
 #include "fa_walk.hpp"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -157,16 +159,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     kdma.load(Kh, N, walk.tile_start(0), kbuf);
     vdma.load(Vh, N, walk.tile_start(0), vbuf);
   }
-  for (int j = 0; j < ntiles; ++j) {
+  // One 64-key tile j held in LDS stage STG.  The walk is unrolled by two
+  // tiles so the stage is a compile-time constant and every LDS address a
+  // per-lane base plus an immediate.
+  auto tile_step = [&](int j, auto stg) {
+    constexpr int STG = decltype(stg)::value;
     wait_loads();
     __syncthreads();
     if (j + 1 < ntiles) {
       const int nxt = walk.tile_start(j + 1);
-      kdma.load(Kh, N, nxt, kbuf + ((j + 1) & 1) * C::TILE);
-      vdma.load(Vh, N, nxt, vbuf + ((j + 1) & 1) * C::TILE);
+      kdma.load(Kh, N, nxt, kbuf + (1 - STG) * C::TILE);
+      vdma.load(Vh, N, nxt, vbuf + (1 - STG) * C::TILE);
     }
-    const unsigned char* kt = kbuf + (j & 1) * C::TILE;
-    const unsigned char* vt = vbuf + (j & 1) * C::TILE;
+    const unsigned char* kt = kbuf + STG * C::TILE;
+    const unsigned char* vt = vbuf + STG * C::TILE;
     const int k0 = walk.tile_start(j);
 
     // S^T of the two 32-key sub-blocks: register r of lane half h = key k0 + 32 sb + 16 h + r
@@ -243,6 +249,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       }
       mma8(acc[nb], va, pk);
     }
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    tile_step(j, std::integral_constant<int, 0>());
+    if (j + 1 < ntiles) tile_step(j + 1, std::integral_constant<int, 1>());
   }
 
   const float l_tot = sum_halves(l_run);
