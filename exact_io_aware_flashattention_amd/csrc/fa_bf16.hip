@@ -343,30 +343,21 @@ struct DkdvB {
   static constexpr int VRES = CELL * BTile<D>::ROWB;    // V of the work-group's 128 keys
   static constexpr int SSTEPS = D / 16;
   static constexpr int NB = D / 32;
-  // d = 256 runs passes 1 and 2 (below); d = 160 fits one pass in one
-  // wave's 512 registers (436, no spill; 5 % faster than two passes)
-  static constexpr bool TWO_PASS = D > 160;
-  // waves per SIMD: d > 128 holds one wave per SIMD, except the dV pass,
-  // which keeps no V tile in LDS (two work-groups fit) and needs only the dV
-  // accumulators
-  static constexpr int occ(int pass) { return D > 128 ? (TWO_PASS && pass == 1 ? 2 : 1) : 2; }
+  // waves per SIMD: above d = 128 one wave holds dK, dV (up to 256
+  // accumulator registers at d = 256) and K in its 512 registers
+  static constexpr int OCC = D > 128 ? 1 : 2;
 };
 
 // SPLIT (block mask present): work-groups [0, SPLIT_MAX_ITEMS) take the split
 // items of the plan (a chunk of a long column each; surplus ones exit), the
 // rest take one column each and exit if the column is split.
-// PASS: 0 accumulates dK and dV together; 1 only dV (S, P); 2 only dK (S, dP,
-// dS).  d = 256 runs passes 1 and 2: there dK and dV together would need
-// 256 accumulator registers per lane besides K's 64, more than one wave holds
-// without spilling; each pass holds half, for one more Q K^T product.
-template <int D, int MODE, bool SPLIT, int PASS = 0>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DkdvB<D>::occ(PASS), DkdvB<D>::occ(PASS)))) void
+template <int D, int MODE, bool SPLIT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DkdvB<D>::OCC, DkdvB<D>::OCC))) void
 dkdv_bf16_kernel(AttnArgs a) {
   using C = DkdvB<D>;
   constexpr bool WALK_ONLY = MODE == K_WALK, DROP = MODE == K_DROP;
-  constexpr bool DO_DV = PASS != 2, DO_DK = PASS != 1;
   __shared__ u32x4 drop_xch[DROP ? NT : 1];
-  constexpr int VRES = DO_DK ? C::VRES : 0;   // the dV pass reads no V
+  constexpr int VRES = C::VRES;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[WALK_ONLY ? 16 : VRES + 2 * C::STAGE];
   __shared__ int cell_list[MAX_T];
   __shared__ int scratch4[4];
@@ -429,13 +420,13 @@ dkdv_bf16_kernel(AttnArgs a) {
       kf[s] = myk < N ? ld16(Kg + (size_t)myk * D + s * 16 + 8 * h) : u32x4{0, 0, 0, 0};
     // d = 64: the wave's V rows stay in registers (16 per lane) after the
     // first tile, instead of being read from LDS for every 32 queries
-    constexpr bool VREG = D == 64 && DO_DK;
+    constexpr bool VREG = D == 64;
     u32x4 vfr[VREG ? C::SSTEPS : 1];
-    f32x16 dk[DO_DK ? C::NB : 1], dv[DO_DV ? C::NB : 1];
+    f32x16 dk[C::NB], dv[C::NB];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
-      if constexpr (DO_DK) zero(dk[nb]);
-      if constexpr (DO_DV) zero(dv[nb]);
+      zero(dk[nb]);
+      zero(dv[nb]);
     }
 
     float st_l = 0.f, st_d = 0.f;   // this thread's row statistics of the next tile
@@ -452,7 +443,7 @@ dkdv_bf16_kernel(AttnArgs a) {
       }
     };
     if (walk.ntiles > 0) {
-      if constexpr (DO_DK) TileDma<D, CELL>().load(reinterpret_cast<const bf16*>(a.v) + head, N, kj * CELL, Vs);
+      TileDma<D, CELL>().load(reinterpret_cast<const bf16*>(a.v) + head, N, kj * CELL, Vs);
       issue(0);
     }
 
@@ -502,9 +493,8 @@ dkdv_bf16_kernel(AttnArgs a) {
 #pragma unroll
           for (int k = 0; k < C::SSTEPS; ++k) {
             mma(s, as_bf16x8(row_chunk<D>(Qs, 32 * qs + l32, 2 * k + h)), as_bf16x8(kf[k]));
-            if constexpr (DO_DK)
-              mma(dp, as_bf16x8(row_chunk<D>(dOs, 32 * qs + l32, 2 * k + h)),
-                  as_bf16x8(VREG ? vfr[k] : row_chunk<D>(Vs, wave * 32 + l32, 2 * k + h)));
+            mma(dp, as_bf16x8(row_chunk<D>(dOs, 32 * qs + l32, 2 * k + h)),
+                as_bf16x8(VREG ? vfr[k] : row_chunk<D>(Vs, wave * 32 + l32, 2 * k + h)));
           }
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -512,26 +502,22 @@ dkdv_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[4 * g + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], a.c, -l4[e]));
           }
-          if constexpr (DO_DV) {
-            const PackedB pb = pack_bf16(s);
+          const PackedB pb = pack_bf16(s);
 #pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb)
+          for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-              for (int mm = 0; mm < 2; ++mm) mma(dv[nb], tr_operand<D>(dOs, 32 * qs + 16 * mm, 32 * nb), pb.p[mm]);
+            for (int mm = 0; mm < 2; ++mm) mma(dv[nb], tr_operand<D>(dOs, 32 * qs + 16 * mm, 32 * nb), pb.p[mm]);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(stats + C::BQ + 32 * qs + 8 * g + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[4 * g + e] = s[4 * g + e] * (dp[4 * g + e] - d4[e]);
           }
-          if constexpr (DO_DK) {
+          const PackedB db = pack_bf16(dp);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x4 d4 = *reinterpret_cast<const f32x4*>(stats + C::BQ + 32 * qs + 8 * g + 4 * h);
+          for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) dp[4 * g + e] = s[4 * g + e] * (dp[4 * g + e] - d4[e]);
-            }
-            const PackedB db = pack_bf16(dp);
-#pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-              for (int mm = 0; mm < 2; ++mm) mma(dk[nb], tr_operand<D>(Qs, 32 * qs + 16 * mm, 32 * nb), db.p[mm]);
-          }
+            for (int mm = 0; mm < 2; ++mm) mma(dk[nb], tr_operand<D>(Qs, 32 * qs + 16 * mm, 32 * nb), db.p[mm]);
         }
         return;
       }
@@ -546,9 +532,8 @@ dkdv_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int k = 0; k < C::SSTEPS; ++k) {
           mma(s, as_bf16x8(row_chunk<D>(Qs, 32 * qs + l32, 2 * k + h)), as_bf16x8(kf[k]));
-          if constexpr (DO_DK)
-            mma(dp, as_bf16x8(row_chunk<D>(dOs, 32 * qs + l32, 2 * k + h)),
-                as_bf16x8(VREG ? vfr[k] : row_chunk<D>(Vs, wave * 32 + l32, 2 * k + h)));
+          mma(dp, as_bf16x8(row_chunk<D>(dOs, 32 * qs + l32, 2 * k + h)),
+              as_bf16x8(VREG ? vfr[k] : row_chunk<D>(Vs, wave * 32 + l32, 2 * k + h)));
         }
         // P = exp2(s c - lse log2 e), dS = P (dP - delta); register r <-> query
         // q0 + 32 qs + acc_row(r, h).  On edge tiles an entry is masked iff the
@@ -576,9 +561,9 @@ dkdv_bf16_kernel(AttnArgs a) {
               // dV uses P Z (the 1 / (1 - p) factor is applied at the end);
               // dS = P ((dO V^T) Z - delta)
               const bool keep = keep_byte(keepw[g], e, a.drop_t);
-              if constexpr (DO_DK) dp[r] = s[r] * ((keep ? dp[r] * a.drop_inv : 0.f) - d4[e]);
+              dp[r] = s[r] * ((keep ? dp[r] * a.drop_inv : 0.f) - d4[e]);
               if (!keep) s[r] = 0.f;
-            } else if constexpr (DO_DK) {
+            } else {
               dp[r] = s[r] * (dp[r] - d4[e]);
             }
           }
@@ -590,28 +575,14 @@ dkdv_bf16_kernel(AttnArgs a) {
             if (acc_row(r, 0) < lim) s[r] = dp[r] = 0.f;
         }
         // dV^T += dO^T P and dK^T += Q^T dS, the transposed operands read from the row-major tiles
-        if constexpr (PASS == 0) {
-          const PackedB pb = pack_bf16(s), db = pack_bf16(dp);
+        const PackedB pb = pack_bf16(s), db = pack_bf16(dp);
 #pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb)
+        for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-            for (int mm = 0; mm < 2; ++mm) {
-              mma(dv[nb], tr_operand<D>(dOs, 32 * qs + 16 * mm, 32 * nb), pb.p[mm]);
-              mma(dk[nb], tr_operand<D>(Qs, 32 * qs + 16 * mm, 32 * nb), db.p[mm]);
-            }
-        } else if constexpr (DO_DV) {
-          const PackedB pb = pack_bf16(s);
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-            for (int mm = 0; mm < 2; ++mm) mma(dv[nb], tr_operand<D>(dOs, 32 * qs + 16 * mm, 32 * nb), pb.p[mm]);
-        } else {
-          const PackedB db = pack_bf16(dp);
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-            for (int mm = 0; mm < 2; ++mm) mma(dk[nb], tr_operand<D>(Qs, 32 * qs + 16 * mm, 32 * nb), db.p[mm]);
-        }
+          for (int mm = 0; mm < 2; ++mm) {
+            mma(dv[nb], tr_operand<D>(dOs, 32 * qs + 16 * mm, 32 * nb), pb.p[mm]);
+            mma(dk[nb], tr_operand<D>(Qs, 32 * qs + 16 * mm, 32 * nb), db.p[mm]);
+          }
       }
     };
     using RT = std::integral_constant<int, -1>;
@@ -655,12 +626,10 @@ dkdv_bf16_kernel(AttnArgs a) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const size_t o = ((size_t)(8 * nb + 2 * g + h) * CELL + kl) * 4;
-            if constexpr (DO_DK)
-              *reinterpret_cast<f32x4*>(slot + o) =
-                  f32x4{dk[nb][4 * g], dk[nb][4 * g + 1], dk[nb][4 * g + 2], dk[nb][4 * g + 3]};
-            if constexpr (DO_DV)
-              *reinterpret_cast<f32x4*>(slot + CELL * D + o) =
-                  f32x4{dv[nb][4 * g], dv[nb][4 * g + 1], dv[nb][4 * g + 2], dv[nb][4 * g + 3]};
+            *reinterpret_cast<f32x4*>(slot + o) =
+                f32x4{dk[nb][4 * g], dk[nb][4 * g + 1], dk[nb][4 * g + 2], dk[nb][4 * g + 3]};
+            *reinterpret_cast<f32x4*>(slot + CELL * D + o) =
+                f32x4{dv[nb][4 * g], dv[nb][4 * g + 1], dv[nb][4 * g + 2], dv[nb][4 * g + 3]};
           }
         __threadfence();   // release this thread's partials at device scope
         __syncthreads();
@@ -671,8 +640,8 @@ dkdv_bf16_kernel(AttnArgs a) {
         // the last chunk adds all partials of the column in chunk order
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
-          if constexpr (DO_DK) zero(dk[nb]);
-          if constexpr (DO_DV) zero(dv[nb]);
+          zero(dk[nb]);
+          zero(dv[nb]);
         }
         for (int c = 0; c < nchunk; ++c) {
           const float* sl = a.split.slots + (size_t)(first + c) * (2 * CELL * D);
@@ -681,15 +650,12 @@ dkdv_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const size_t o = ((size_t)(8 * nb + 2 * g + h) * CELL + kl) * 4;
-              if constexpr (DO_DK) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(sl + o);
+              const f32x4 x = *reinterpret_cast<const f32x4*>(sl + o);
+              const f32x4 y = *reinterpret_cast<const f32x4*>(sl + CELL * D + o);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dk[nb][4 * g + e] += x[e];
-              }
-              if constexpr (DO_DV) {
-                const f32x4 y = *reinterpret_cast<const f32x4*>(sl + CELL * D + o);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dv[nb][4 * g + e] += y[e];
+              for (int e = 0; e < 4; ++e) {
+                dk[nb][4 * g + e] += x[e];
+                dv[nb][4 * g + e] += y[e];
               }
             }
         }
@@ -703,13 +669,11 @@ dkdv_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int c = 32 * nb + 8 * g + 4 * h;
-          if constexpr (DO_DK)
-            store4(dkp + c, dk[nb][4 * g] * a.scale, dk[nb][4 * g + 1] * a.scale, dk[nb][4 * g + 2] * a.scale,
-                   dk[nb][4 * g + 3] * a.scale);
+          store4(dkp + c, dk[nb][4 * g] * a.scale, dk[nb][4 * g + 1] * a.scale, dk[nb][4 * g + 2] * a.scale,
+                 dk[nb][4 * g + 3] * a.scale);
           const float vs = DROP ? a.drop_inv : 1.f;
-          if constexpr (DO_DV)
-            store4(dvp + c, dv[nb][4 * g] * vs, dv[nb][4 * g + 1] * vs, dv[nb][4 * g + 2] * vs,
-                   dv[nb][4 * g + 3] * vs);
+          store4(dvp + c, dv[nb][4 * g] * vs, dv[nb][4 * g + 1] * vs, dv[nb][4 * g + 2] * vs,
+                 dv[nb][4 * g + 3] * vs);
         }
     }
   }
@@ -944,12 +908,12 @@ FA_DEFINE_LAUNCH(launch_dq_b, dq_bf16_kernel)
 
 // dK/dV: with a block mask the split plan runs first and SPLIT_MAX_ITEMS
 // work-groups for split items precede the per-column ones.
-template <int D, int PASS>
-static hipError_t launch_dkdv_pass(const AttnArgs& a, bool walk_only, hipStream_t s) {
+template <int D>
+static hipError_t launch_dkdv_b(const AttnArgs& a, bool walk_only, hipStream_t s) {
   const long long ncol = (long long)((a.N + CELL - 1) / CELL) * a.H * a.B;
   const long long nwg = a.mask ? SPLIT_MAX_ITEMS + ncol : ncol;
   if (a.mask) {
-    // (the plan also clears the arrival counters, so every pass gets its own)
+    // (the plan also clears the arrival counters)
     const hipError_t e = launch_split_plan(a, s);
     if (e != hipSuccess) return e;
   }
@@ -961,34 +925,18 @@ static hipError_t launch_dkdv_pass(const AttnArgs& a, bool walk_only, hipStream_
       hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_WALK, false>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  if constexpr (DkdvB<D>::TWO_PASS && PASS == 0) {
-    return hipErrorInvalidValue;   // d = 256 computes in passes 1 and 2 only
+  if (a.mask) {
+    if (a.drop_t)
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_DROP, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_PLAIN, true>), grid, block, 0, s, a);
   } else {
-    if (a.mask) {
-      if (a.drop_t)
-        hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_DROP, true, PASS>), grid, block, 0, s, a);
-      else
-        hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_PLAIN, true, PASS>), grid, block, 0, s, a);
-    } else {
-      if (a.drop_t)
-        hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_DROP, false, PASS>), grid, block, 0, s, a);
-      else
-        hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_PLAIN, false, PASS>), grid, block, 0, s, a);
-    }
-    return hipGetLastError();
+    if (a.drop_t)
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_DROP, false>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((dkdv_bf16_kernel<D, K_PLAIN, false>), grid, block, 0, s, a);
   }
-}
-
-template <int D>
-static hipError_t launch_dkdv_b(const AttnArgs& a, bool walk_only, hipStream_t s) {
-  if constexpr (DkdvB<D>::TWO_PASS) {
-    if (walk_only) return launch_dkdv_pass<D, 0>(a, true, s);
-    const hipError_t e = launch_dkdv_pass<D, 1>(a, false, s);
-    if (e != hipSuccess) return e;
-    return launch_dkdv_pass<D, 2>(a, false, s);
-  } else {
-    return launch_dkdv_pass<D, 0>(a, walk_only, s);
-  }
+  return hipGetLastError();
 }
 
 // Merge of the key ranges of a split-key forward (one thread per row and four

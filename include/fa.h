@@ -30,10 +30,9 @@
  *              Attention", Flash Attention 2, "Dukungan untuk dimensi head
  *              yang lebih besar").  Above d = 128 a work-group's tiles fill
  *              the LDS and its accumulators a whole wave's registers, so one
- *              wave runs per SIMD; at d = 256 dK/dV are accumulated in two
- *              passes over the queries (dV, then dK), which costs one more
- *              Q K^T product.  d = 96 and 160 are staged in LDS as rows of 128 and
- *              256 columns, and need N * d <= 2^30 (else FA_ERR_SHAPE).
+ *              wave runs per SIMD.  d = 96 and 160 are staged in LDS as rows
+ *              of 128 and 256 columns, and need N * d <= 2^30 (else
+ *              FA_ERR_SHAPE).
  *   scale      finite and > 0 (the pages write S = QK^T, i.e. scale = 1).
  *   causal     nonzero: key j is allowed for query i only if j <= i (queries
  *              and keys share positions, top-left aligned).

@@ -190,7 +190,7 @@ def test_dropout_full_size_sampled():
 def test_dropout_split_key_column(d):
     """Dropout with a block mask whose key columns are split over work-groups
     in dK/dV (chunk 16 cells, set columns visited by 40 query cells): the
-    split partial sums and, at d = 256, both dK/dV passes with their own plans."""
+    split partial sums, at d = 64 and at d = 256."""
     from test_parity import split_mask
     N = 40 * 128 - 37
     T = -(-N // 128)

@@ -1,8 +1,8 @@
 """GPU parity at head dimension 256 (bf16 only).
 
-At d = 256 the kernels run one wave per SIMD and dK/dV are accumulated in two
-passes (dV, then dK), each with its own block-sparse split plan; these cases
-cover that path against the fp64 oracle: plain, causal, key padding, both
+At d = 256 the kernels run one wave per SIMD, dK and dV together taking up to
+256 accumulator registers of the wave; these cases cover that path against the
+fp64 oracle: plain, causal, key padding, both
 mask kinds, a split key column, dropout, the split-key forward (decoding and
 matrix-core paths), and the 16K long-context shape at full size on sampled
 rows and key columns."""
@@ -47,9 +47,8 @@ def test_d256_parity(case):
 
 def test_d256_split_key_column():
     """A key column visited by 18 query cells (more than the chunk of 16) is
-    split over work-groups in both dK/dV passes; each pass has its own plan and
-    counters.  Element-wise against the dense oracle, and bit-identical on a
-    repeat."""
+    split over work-groups in dK/dV, with the split plan and its counters.
+    Element-wise against the dense oracle, and bit-identical on a repeat."""
     N = 18 * 128 - 95
     bm = split_mask(18, 2300, 9)
     inp = small_inputs(1, 2, N, 256, "bf16", False, mask=bm, seed=2301)

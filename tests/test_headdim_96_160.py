@@ -5,7 +5,7 @@ with rows of the next power of two (128, 256), filling the pad chunks with
 zeros from past the end of the buffer, and the decoding kernel serves a key
 row with a power-of-two group of lanes whose extra lanes read zeros.  d = 96
 runs like d = 128 (two waves per SIMD, dK and dV together); d = 160 like
-d = 256 (one wave per SIMD, dK/dV in two passes).  Cases, against the fp64
+d = 256 (one wave per SIMD).  Cases, against the fp64
 oracle: plain, causal, key padding, both mask kinds, ragged N, a split key
 column, dropout, the split-key forward (decoding and matrix-core paths) and
 decoding against an E4M3 key/value cache."""
