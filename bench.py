@@ -373,7 +373,7 @@ def cpu_baseline(w, inp, heads=6):
 
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "long_context_hbm_traffic.txt")
-KERNEL_SYMBOL = {"fwd": "fwd_bf16_kernel<128, 0>", "dkdv": "dkdv_bf16_kernel<128, 0, false, 0>",
+KERNEL_SYMBOL = {"fwd": "fwd_bf16_kernel<128, 0>", "dkdv": "dkdv_bf16_kernel<128, 0, false>",
                  "dq": "dq_bf16_kernel<128, 0>", "pre": "bwd_pre_kernel"}
 
 
