@@ -431,7 +431,7 @@ def summarize_counters(fetch_csv, write_csv, command):
         fn = [n for n in fetch if sym in n or (key == "pre" and "bwd_pre" in n)]
         wn = [n for n in write if sym in n or (key == "pre" and "bwd_pre" in n)]
         if not fn or not wn:
-            continue
+            raise SystemExit(f"no {key} kernel ({sym}) in the counter files; kernel names: {sorted(fetch)}")
         fb = statistics.median(fetch[fn[0]]) * 1024 * f_scale
         wb = statistics.median(write[wn[0]]) * 1024 * w_scale
         lines += [f"fetch_{key} = {fb:.0f}", f"write_{key} = {wb:.0f}", f"bytes_{key} = {fb + wb:.0f}"]
