@@ -73,3 +73,19 @@ def test_splitkv_pairs_and_bounds():
     assert b == 2 * 256 * (2 + 2 * 16384) * 128 + 4 * 256
     f, b = bench.splitkv_alg(SPLITKV_WORKLOADS["prefill"])
     assert f / b > ridge
+
+
+def test_profiled_kernel_names_exist_in_the_library():
+    """The counter summary finds each kernel of the long-context step by the name
+    rocprofv3 reports; every name bench.py looks for must be a kernel of the
+    built library (a renamed template would otherwise drop out of the traffic
+    figures)."""
+    import shutil
+
+    import pytest
+    lib = os.path.join(ROOT, "exact_io_aware_flashattention_amd", "libfa.so")
+    if not os.path.exists(lib) or shutil.which("nm") is None:
+        pytest.skip("libfa.so not built or nm not available")
+    syms = subprocess.run(["nm", "-C", lib], stdout=subprocess.PIPE, text=True, check=True).stdout
+    for key, sym in bench.KERNEL_SYMBOL.items():
+        assert sym in syms, f"{key}: no kernel named {sym} in libfa.so"
