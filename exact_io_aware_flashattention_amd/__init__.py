@@ -111,14 +111,62 @@ def _shape(t):
     return tuple(int(x) for x in t.shape)
 
 
-def _check_like(ref, *ts):
-    for t in ts:
-        if t is None:
-            continue
-        if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous [B, H, N, d]")
-        if t.device != ref.device:
-            raise ValueError("all tensors must be on the same device")
+# The C ABI receives bare pointers and cannot see how large an allocation is:
+# every tensor is checked here, before any library call, for the device, the
+# dtype, the shape and the layout the kernels assume.  A mismatch raises
+# TypeError (dtype) or ValueError (anything else).
+
+def _on_gpu(name, t, ref):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if t.device != ref.device:
+        raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _like(name, t, shape, dtype):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _validate(ref, specs):
+    """specs: (name, tensor or None, shape, dtype).  Dtypes and shapes are
+    checked first, then that every tensor (and ref) is a contiguous GPU tensor
+    on ref's device."""
+    live = [(n, t, s, dt) for n, t, s, dt in specs if t is not None]
+    for n, t, s, dt in live:
+        _like(n, t, s, dt)
+    for n, t, _, _ in live:
+        _on_gpu(n, t, ref)
+
+
+def _mask_specs(B, N, block_mask, kv_len):
+    import torch
+    T = -(-N // CELL)
+    return [("block_mask", block_mask, (T, T), torch.uint8), ("kv_len", kv_len, (B,), torch.int32)]
+
+
+def _workspace_spec(workspace):
+    import torch
+    if workspace is not None and workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    return [("workspace", workspace, tuple(workspace.shape) if workspace is not None else (), torch.uint8)]
+
+
+def _check_square(q, named, B, H, N, block_mask=None, kv_len=None, stats=(), workspace=None):
+    """q: [B,H,N,d] bf16/f32 on the GPU; every tensor of ``named`` has q's shape
+    and dtype; every tensor of ``stats`` is float32 [B,H,N]."""
+    import torch
+    _dtype_code(q)
+    specs = [("q", q, q.shape, q.dtype)] + [(n, t, q.shape, q.dtype) for n, t in named]
+    specs += [(n, t, (B, H, N), torch.float32) for n, t in stats]
+    _validate(q, specs + _mask_specs(B, N, block_mask, kv_len) + _workspace_spec(workspace))
 
 
 def _call(name, *args):
@@ -137,6 +185,11 @@ def _scale(scale, d):
 
 # ---------------------------------------------------------------- entry points
 
+def _new(shape, dtype, ref):
+    import torch
+    return torch.empty(shape, dtype=dtype, device=ref.device)
+
+
 def fa_fwd(q, k, v, o=None, lse=None, *, scale=None, causal=False, block_mask=None, kv_len=None,
            dropout_p=0.0, seed=0, stream=None):
     """O, lse = attention forward.  q, k, v: [B,H,N,d] bf16 or float32 on the GPU;
@@ -145,11 +198,9 @@ def fa_fwd(q, k, v, o=None, lse=None, *, scale=None, causal=False, block_mask=No
     of 1/256) with the Philox stream of `seed`."""
     import torch
     B, H, N, d = _shape(q)
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    _check_like(q, q, k, v, o, lse, block_mask, kv_len)
+    _check_square(q, [("k", k), ("v", v), ("o", o)], B, H, N, block_mask, kv_len, [("lse", lse)])
+    o = _new(q.shape, q.dtype, q) if o is None else o
+    lse = _new((B, H, N), torch.float32, q) if lse is None else lse
     mb, kl = _mask_args(block_mask, kv_len)
     if dropout_p:
         _call("fa_fwd_dropout", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _scale(scale, d),
@@ -160,23 +211,28 @@ def fa_fwd(q, k, v, o=None, lse=None, *, scale=None, causal=False, block_mask=No
     return o, lse
 
 
+def _check_split(q, k, v, o, lse, kv_len, kv_dtype, workspace):
+    """q: bf16 [B,H,Nq,d]; k, v: kv_dtype [B,H,Nk,d]; o like q; lse f32 [B,H,Nq]."""
+    import torch
+    B, H, Nq, d = _shape(q)
+    _, _, Nk, _ = _shape(k)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("the split-key forward takes bfloat16 queries")
+    _validate(q, [("q", q, q.shape, q.dtype), ("k", k, (B, H, Nk, d), kv_dtype), ("v", v, (B, H, Nk, d), kv_dtype),
+                  ("o", o, q.shape, q.dtype), ("lse", lse, (B, H, Nq), torch.float32),
+                  ("kv_len", kv_len, (B,), torch.int32)] + _workspace_spec(workspace))
+    return B, H, Nq, Nk, d
+
+
 def fa_fwd_splitkv_fp8kv(q, k8, v8, k_descale, v_descale, o=None, lse=None, *, scale=None, causal=False,
                          kv_len=None, num_splits=0, workspace=None, stream=None):
     """Decoding (at most 4 bf16 queries [B,H,Nq,d]) against E4M3 K and V codes
     (uint8 [B,H,Nk,d]; real value = code * descale), keys split over ranges
     as fa_fwd_splitkv."""
     import torch
-    B, H, Nq, d = _shape(q)
-    Bk, Hk, Nk, dk = _shape(k8)
-    if (Bk, Hk, dk) != (B, H, d) or tuple(v8.shape) != tuple(k8.shape):
-        raise ValueError("k8 and v8 must be [B, H, Nk, d] with q's B, H and d")
-    if k8.dtype != torch.uint8 or v8.dtype != torch.uint8:
-        raise TypeError("K and V are uint8 tensors of E4M3 codes")
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    _check_like(q, q, k8, v8, o, lse, kv_len)
+    B, H, Nq, Nk, d = _check_split(q, k8, v8, o, lse, kv_len, torch.uint8, workspace)
+    o = _new(q.shape, q.dtype, q) if o is None else o
+    lse = _new((B, H, Nq), torch.float32, q) if lse is None else lse
     ws, nbytes = _workspace(workspace, fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits), q.device)
     _call("fa_fwd_splitkv_fp8kv", _ptr(q), _ptr(k8) if Nk else None, _ptr(v8) if Nk else None, _ptr(o), _ptr(lse),
           B, H, Nq, Nk, d, _scale(scale, d), int(bool(causal)), _ptr(kv_len), float(k_descale), float(v_descale),
@@ -190,14 +246,13 @@ def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o=None, lse=None, *,
     OCP E4M3 codes whose real values are code * descale (one float per tensor)."""
     import torch
     B, H, N, d = _shape(q8)
-    for t in (q8, k8, v8):
-        if t.dtype != torch.uint8:
-            raise TypeError("FP8 inputs are uint8 tensors of E4M3 codes")
-    if o is None:
-        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
-    _check_like(q8, q8, k8, v8, o, lse, block_mask, kv_len)
+    if q8.dtype != torch.uint8:
+        raise TypeError("FP8 inputs are uint8 tensors of E4M3 codes")
+    _validate(q8, [("q8", q8, q8.shape, torch.uint8), ("k8", k8, q8.shape, torch.uint8),
+                   ("v8", v8, q8.shape, torch.uint8), ("o", o, q8.shape, torch.bfloat16),
+                   ("lse", lse, (B, H, N), torch.float32)] + _mask_specs(B, N, block_mask, kv_len))
+    o = _new((B, H, N, d), torch.bfloat16, q8) if o is None else o
+    lse = _new((B, H, N), torch.float32, q8) if lse is None else lse
     mb, kl = _mask_args(block_mask, kv_len)
     _call("fa_fwd_fp8", _ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, H, N, d, _scale(scale, d),
           int(bool(causal)), mb, kl, float(q_descale), float(k_descale), float(v_descale), _stream(stream))
@@ -236,15 +291,9 @@ def fa_fwd_splitkv(q, k, v, o=None, lse=None, *, scale=None, causal=False, kv_le
     whose partial results are merged.  causal aligns the queries with the
     last Nq key positions (key j allowed for query i iff j <= i + Nk - Nq)."""
     import torch
-    B, H, Nq, d = _shape(q)
-    Bk, Hk, Nk, dk = _shape(k)
-    if (Bk, Hk, dk) != (B, H, d) or tuple(v.shape) != tuple(k.shape):
-        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    _check_like(q, q, k, v, o, lse, kv_len)
+    B, H, Nq, Nk, d = _check_split(q, k, v, o, lse, kv_len, torch.bfloat16, workspace)
+    o = _new(q.shape, q.dtype, q) if o is None else o
+    lse = _new((B, H, Nq), torch.float32, q) if lse is None else lse
     ws, nbytes = _workspace(workspace, fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits), q.device)
     _call("fa_fwd_splitkv", _ptr(q), _ptr(k) if Nk else None, _ptr(v) if Nk else None, _ptr(o), _ptr(lse), B, H,
           Nq, Nk, d, _scale(scale, d), int(bool(causal)), _ptr(kv_len), _dtype_code(q), int(num_splits), _ptr(ws),
@@ -256,14 +305,14 @@ def fa_bwd(q, k, v, o, dO, lse, dq=None, dk=None, dv=None, *, scale=None, causal
            kv_len=None, dropout_p=0.0, seed=0, workspace=None, stream=None):
     """dQ, dK, dV for the loss gradient dO, from the forward's O and lse (with
     the same dropout_p and seed as the forward)."""
-    import torch
     B, H, N, d = _shape(q)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    _check_square(q, [("k", k), ("v", v), ("o", o), ("dO", dO), ("dq", dq), ("dk", dk), ("dv", dv)],
+                  B, H, N, block_mask, kv_len, [("lse", lse)], workspace)
+    dq = _new(q.shape, q.dtype, q) if dq is None else dq
+    dk = _new(q.shape, q.dtype, q) if dk is None else dk
+    dv = _new(q.shape, q.dtype, q) if dv is None else dv
     need = fa_bwd_workspace_bytes(B, H, N, d, _dtype_code(q), block_mask is not None)
     workspace, ws_bytes = _workspace(workspace, max(need, 256), q.device)
-    _check_like(q, q, k, v, o, dO, lse, dq, dk, dv, workspace, block_mask, kv_len)
     mb, kl = _mask_args(block_mask, kv_len)
     if dropout_p:
         _call("fa_bwd_dropout", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
@@ -279,22 +328,22 @@ def fa_bwd(q, k, v, o, dO, lse, dq=None, dk=None, dv=None, *, scale=None, causal
 def fa_bwd_preprocess(o, dO, delta=None, *, stream=None):
     import torch
     B, H, N, d = _shape(o)
-    if delta is None:
-        delta = torch.empty((B, H, N), dtype=torch.float32, device=o.device)
-    _check_like(o, o, dO, delta)
+    _dtype_code(o)
+    _validate(o, [("o", o, o.shape, o.dtype), ("dO", dO, o.shape, o.dtype), ("delta", delta, (B, H, N), torch.float32)])
+    delta = _new((B, H, N), torch.float32, o) if delta is None else delta
     _call("fa_bwd_preprocess", _ptr(o), _ptr(dO), _ptr(delta), B, H, N, d, _dtype_code(o), _stream(stream))
     return delta
 
 
 def fa_bwd_dkdv(q, k, v, dO, lse, delta, dk=None, dv=None, *, scale=None, causal=False, block_mask=None,
                 kv_len=None, workspace=None, stream=None):
-    import torch
     B, H, N, d = _shape(q)
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    _check_square(q, [("k", k), ("v", v), ("dO", dO), ("dk", dk), ("dv", dv)], B, H, N,
+                  block_mask, kv_len, [("lse", lse), ("delta", delta)], workspace)
+    dk = _new(q.shape, q.dtype, q) if dk is None else dk
+    dv = _new(q.shape, q.dtype, q) if dv is None else dv
     need = fa_bwd_dkdv_workspace_bytes(N, d, _dtype_code(q), block_mask is not None)
     workspace, ws_bytes = _workspace(workspace, need, q.device)
-    _check_like(q, q, k, v, dO, lse, delta, dk, dv, workspace, block_mask, kv_len)
     mb, kl = _mask_args(block_mask, kv_len)
     _call("fa_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(dk), _ptr(dv),
           B, H, N, d, _scale(scale, d), int(bool(causal)), mb, kl, _dtype_code(q), _ptr(workspace), ws_bytes,
@@ -304,10 +353,10 @@ def fa_bwd_dkdv(q, k, v, dO, lse, delta, dk=None, dv=None, *, scale=None, causal
 
 def fa_bwd_dq(q, k, v, dO, lse, delta, dq=None, *, scale=None, causal=False, block_mask=None, kv_len=None,
               stream=None):
-    import torch
     B, H, N, d = _shape(q)
-    dq = torch.empty_like(q) if dq is None else dq
-    _check_like(q, q, k, v, dO, lse, delta, dq, block_mask, kv_len)
+    _check_square(q, [("k", k), ("v", v), ("dO", dO), ("dq", dq)], B, H, N, block_mask, kv_len,
+                  [("lse", lse), ("delta", delta)])
+    dq = _new(q.shape, q.dtype, q) if dq is None else dq
     mb, kl = _mask_args(block_mask, kv_len)
     _call("fa_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(dq),
           B, H, N, d, _scale(scale, d), int(bool(causal)), mb, kl, _dtype_code(q), _stream(stream))
@@ -321,6 +370,7 @@ def fa_debug_visits(which, B, H, N, d, *, causal=False, block_mask=None, kv_len=
     import torch
     T = -(-N // CELL)
     counts = torch.zeros((B, T, T), dtype=torch.int32, device=device)
+    _validate(counts, _mask_specs(B, N, block_mask, kv_len) + _workspace_spec(workspace))
     need = fa_bwd_dkdv_workspace_bytes(N, d, dtype, block_mask is not None) if which == WALK_DKDV else 0
     workspace, ws_bytes = _workspace(workspace, need, device)
     mb, kl = _mask_args(block_mask, kv_len)

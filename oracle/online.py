@@ -10,13 +10,14 @@ f, l and the two-block merge: bornlex.github.io "Flash Attention", section
 merge of m, f and l over x = [x1, x2]); FlashAttention reading guide
 (xyznot.com), "Pelacakan Softmax Inkremental" (the merge of m and l).
 
-Tiled forward: FlashAttention reading guide, "Metode", steps 1-4 -- per query
-block i and key block j: the block scores, the block statistics (row max,
-exp, row sum), the update of the running (m, l), and the update of the running
-output, which is re-normalised at every step.  Scale and masks are added as in
-``attention``.  A block whose rows are all masked so far keeps m = -inf; the
-exponent of (-inf) - (-inf) is taken as 0 weight, i.e. the -inf block adds
-nothing.
+Tiled forward: the key axis of each query block is cut into blocks, and the
+statistics of the whole row are a left fold of the two-block merge above over
+those blocks (reading guide, "Pelacakan Softmax Inkremental"; the per-block
+procedure is the reading guide's "Metode").  The output is carried the same
+way: each block contributes its unnormalised f(x) V, weighted by
+exp(m_block - m), and the row is divided by l once, after the last block.
+Scale and masks are added as in ``attention``.  A block whose entries are all
+masked has m = -inf and weight 0, so it adds nothing.
 """
 from __future__ import annotations
 
@@ -60,8 +61,15 @@ def merge_f(m1, f1, m2, f2):
     return np.concatenate([_w(m1, m)[..., None] * f1, _w(m2, m)[..., None] * f2], axis=-1)
 
 
+def _block_stats(S):
+    """(m, l, F) of one block of masked scores: row max, row sum of f and f itself."""
+    m = S.max(axis=1)
+    F = _w(S, m[:, None])
+    return m, F.sum(axis=1), F
+
+
 def tiled_head_forward(Q, K, V, scale, Br, Bc, causal=False, block_mask=None, kv_len=None):
-    """One (b, h) with the block-by-block update; returns O, m, l ([N,d], [N], [N])."""
+    """One (b, h) folded block by block; returns O, m, l ([N,d], [N], [N])."""
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
@@ -71,26 +79,17 @@ def tiled_head_forward(Q, K, V, scale, Br, Bc, causal=False, block_mask=None, kv
     l_all = np.zeros(N)
     for i0 in range(0, N, Br):
         rows = np.arange(i0, min(N, i0 + Br))
-        Oi = np.zeros((rows.size, V.shape[1]))
-        mi = np.full(rows.size, -np.inf)
-        li = np.zeros(rows.size)
+        ok = allowed(rows, Nk, causal, block_mask, kv_len)
+        m = np.full(rows.size, -np.inf)
+        l = np.zeros(rows.size)
+        acc = np.zeros((rows.size, V.shape[1]))      # unnormalised output, relative to m
         for j0 in range(0, Nk, Bc):
             cols = np.arange(j0, min(Nk, j0 + Bc))
-            # step 1: block scores
-            S = scale * (Q[rows] @ K[cols].T)
-            ok = allowed(rows, Nk, causal, block_mask, kv_len)[:, cols]
-            S = np.where(ok, S, -np.inf)
-            # step 2: block statistics
-            mt = S.max(axis=1)
-            Pt = _w(S, mt[:, None])
-            lt = Pt.sum(axis=1)
-            # step 3: running statistics
-            mn, ln = merge(mi, li, mt, lt)
-            # step 4: running output, normalised by the new l
-            a = _w(mi, mn) * li
-            b = _w(mt, mn)
-            inv = np.where(ln > 0, 1.0 / np.where(ln > 0, ln, 1.0), 0.0)
-            Oi = inv[:, None] * (a[:, None] * Oi + b[:, None] * (Pt @ V[cols]))
-            mi, li = mn, ln
-        O[rows], m_all[rows], l_all[rows] = Oi, mi, li
+            S = np.where(ok[:, cols], scale * (Q[rows] @ K[cols].T), -np.inf)
+            mb, lb, F = _block_stats(S)
+            m_new, l = merge(m, l, mb, lb)
+            acc = _w(m, m_new)[:, None] * acc + _w(mb, m_new)[:, None] * (F @ V[cols])
+            m = m_new
+        inv = np.where(l > 0, 1.0 / np.where(l > 0, l, 1.0), 0.0)
+        O[rows], m_all[rows], l_all[rows] = inv[:, None] * acc, m, l
     return O, m_all, l_all

@@ -347,3 +347,52 @@ def test_offset_causal_is_the_tail_of_the_square_problem():
     Osq2, lsesq2 = attention.head_forward(Qx[Nq - Nk:], K, V, scale, causal=True)
     assert np.allclose(O[Nq - Nk:], Osq2, rtol=1e-13, atol=1e-13)
     assert np.allclose(lse[Nq - Nk:], lsesq2, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- batched backward and row blocks
+
+def _autograd_grads(torch, Q, K, V, dO, scale, ok):
+    """dQ, dK, dV of sum(O * dO) by torch autograd through the CPU fp64
+    scaled_dot_product_attention with a boolean mask (True = allowed)."""
+    t = [torch.tensor(x, requires_grad=True) for x in (Q, K, V)]
+    out = torch.nn.functional.scaled_dot_product_attention(
+        t[0][None], t[1][None], t[2][None], attn_mask=torch.from_numpy(ok), scale=scale)[0]
+    (out * torch.from_numpy(dO)).sum().backward()
+    return [x.grad.numpy() for x in t]
+
+
+def test_batched_backward_per_batch_kv_len_against_autograd(rng):
+    """attention.backward picks kv_len[b] for batch entry b and the block mask
+    for every head: each (b, h) is checked against autograd with that entry's
+    own mask, so a wrong batch index or a dropped mask condition fails."""
+    torch = pytest.importorskip("torch")
+    B, H, N, d, scale = 2, 2, 300, 8, 0.3
+    q, k, v, do = (rand(rng, B, H, N, d) for _ in range(4))
+    kv_len = np.array([150, 300])
+    bm = np.array([[1, 0, 0], [1, 1, 0], [1, 0, 1]], np.uint8)   # first column kept: no empty row
+    dq, dk, dv = attention.backward(q, k, v, do, scale, causal=True, block_mask=bm, kv_len=kv_len)
+    for b in range(B):
+        ok = attention.allowed(np.arange(N), N, True, bm, int(kv_len[b]))
+        assert ok.any(axis=1).all()
+        for h in range(H):
+            ref = _autograd_grads(torch, q[b, h], k[b, h], v[b, h], do[b, h], scale, ok)
+            for got, want in zip((dq[b, h], dk[b, h], dv[b, h]), ref):
+                assert np.abs(got - want).max() < 1e-12
+    # the padded keys of entry 0 get no gradient, those of entry 1 do
+    assert np.all(dk[0, :, 150:] == 0) and np.all(dv[0, :, 150:] == 0)
+    assert np.abs(dv[1, :, 150:]).max() > 0
+
+
+@pytest.mark.parametrize("row_block", [64, 100, 299])
+def test_head_backward_accumulates_across_row_blocks(rng, row_block):
+    """head_backward walks the queries in row blocks and adds every block's
+    contribution to dK and dV: with several blocks (N = 300) it must equal
+    autograd, which a '=' in place of '+=' would break."""
+    torch = pytest.importorskip("torch")
+    N, d, scale = 300, 8, 0.35
+    Q, K, V, dO = (rand(rng, N, d) for _ in range(4))
+    ok = attention.allowed(np.arange(N), N, causal=True, kv_len=270)
+    got = attention.head_backward(Q, K, V, dO, scale, causal=True, kv_len=270, row_block=row_block)
+    ref = _autograd_grads(torch, Q, K, V, dO, scale, ok)
+    for a, b in zip(got, ref):
+        assert np.abs(a - b).max() < 1e-12
