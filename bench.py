@@ -21,8 +21,18 @@ dimension 256) with the same step and
 prints the same kind of line (no CPU leg unless --cpu-baseline is given); the
 default line is the long-context workload.  Per kernel it reports achieved
 TFLOP/s against the bf16 matrix peak and achieved GB/s of compulsory HBM
-traffic against 8 TB/s, and names the bound of each kernel from its
-arithmetic intensity (compulsory bytes) against the ridge point.
+traffic against 8 TB/s ("alg_gbs": compulsory bytes / time, a derived
+figure), and names the bound of each kernel from its arithmetic intensity
+(compulsory bytes) against the ridge point.  Where a counter summary for the
+workload is committed under profiles/ and still matches the kernel sources,
+each kernel also gets "hbm_bytes" (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled
+by a plain copy's readings) and "hbm_gbs" = hbm_bytes / time.
+
+Every per-kernel time is reported as the mean over the timed steps, with the
+median and the minimum beside it.  --cold writes a 512 MiB scrub buffer before
+every timed launch (outside its event bracket), so each kernel starts with its
+operands evicted from L2 and the MALL; the step time is then the sum of the
+kernels' times.
 """
 from __future__ import annotations
 
@@ -75,6 +85,9 @@ def workload_fwd_flops(w, inp):
 
 
 PRODUCTS = {"fwd": 2, "dkdv": 4, "dq": 3, "pre": 0}
+# Products each kernel owes the method (dQ = scale dS K is one product; S and
+# dP are recomputed in the dQ kernel, which the executed count includes).
+ALG_PRODUCTS = {"fwd": 2, "dkdv": 4, "dq": 1, "pre": 0}
 
 
 def kernel_flops(name, f_fwd):
@@ -140,7 +153,10 @@ def run_gpu_bench_dropout(w, steps, warmup, inp, p, seed=2024):
     return start.elapsed_time(end) / steps, per, (B, H, N, d)
 
 
-def run_gpu_bench(w, steps, warmup, inp):
+SCRUB_BYTES = 512 << 20
+
+
+def run_gpu_bench(w, steps, warmup, inp, cold=False):
     import numpy as np
     import torch
 
@@ -160,27 +176,26 @@ def run_gpu_bench(w, steps, warmup, inp):
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev) if ws_bytes else None
     kw = dict(scale=w.scale, causal=w.causal, block_mask=bm, kv_len=kl)
     stream = torch.cuda.current_stream()
+    scrub = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev) if cold else None
+    launches = [lambda: fa.fa_fwd(q, k, v, o, lse, stream=stream, **kw),
+                lambda: fa.fa_bwd_preprocess(o, do, delta, stream=stream),
+                lambda: fa.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, workspace=ws, stream=stream, **kw),
+                lambda: fa.fa_bwd_dq(q, k, v, do, lse, delta, dq, stream=stream, **kw)]
 
     def step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        fa.fa_fwd(q, k, v, o, lse, stream=stream, **kw)
-        if ev:
-            ev[1].record(stream)
-        fa.fa_bwd_preprocess(o, do, delta, stream=stream)
-        if ev:
-            ev[2].record(stream)
-        fa.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, workspace=ws, stream=stream, **kw)
-        if ev:
-            ev[3].record(stream)
-        fa.fa_bwd_dq(q, k, v, do, lse, delta, dq, stream=stream, **kw)
-        if ev:
-            ev[4].record(stream)
+        for j, launch in enumerate(launches):
+            if scrub is not None:
+                scrub.fill_(float(j))     # evict the operands: 512 MiB written through L2 and the MALL
+            if ev:
+                ev[2 * j].record(stream)
+            launch()
+            if ev:
+                ev[2 * j + 1].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -194,13 +209,11 @@ def run_gpu_bench(w, steps, warmup, inp):
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     names = ["fwd", "pre", "dkdv", "dq"]
-    per = {n: 0.0 for n in names}
-    for ev in evs:
-        for j, n in enumerate(names):
-            per[n] += ev[j].elapsed_time(ev[j + 1])
-    per = {n: per[n] / steps for n in names}      # ms per launch
+    samples = {n: [ev[2 * j].elapsed_time(ev[2 * j + 1]) for ev in evs] for j, n in enumerate(names)}
+    per = {n: sum(s) / steps for n, s in samples.items()}      # mean ms per launch
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(dq).all())
-    return total_ms / steps, per, wall, (B, H, N, d)
+    step_ms = sum(per.values()) if cold else total_ms / steps
+    return step_ms, per, wall, (B, H, N, d), samples
 
 
 def splitkv_pairs(Nq, Nk, causal):
@@ -291,7 +304,7 @@ def run_gpu_bench_splitkv(which, steps, warmup, fp8kv=False):
         "config": {"workload": w["desc"] + (", K/V cache in E4M3" if fp8kv else ""), "B": B, "H": H, "Nq": Nq,
                    "Nk": Nk, "d": d, "causal": w["causal"],
                    "num_splits": nsplit, "input_sha256": digest(qa, ka, va)},
-        "call_ms": round(call_ms, 4), "tflops": round(tf, 2), "hbm_gbs": round(gbs, 1),
+        "call_ms": round(call_ms, 4), "tflops": round(tf, 2), "alg_gbs": round(gbs, 1),
         "roofline": roofline}
 
 
@@ -337,6 +350,16 @@ def run_gpu_bench_fp8(w, steps, warmup, inp):
 
 COPY_BYTES = 256 << 20
 
+DESC = {1: "tiny exact: B=1 H=2 N=128 d=64 fp32, scale 1/8",
+        2: "GPT-2 shaped: B=8 H=12 N=1024 d=64 bf16 causal, scale 1/8",
+        3: "BERT-large shaped: B=32 H=16 N=512 d=64 bf16, key padding kv_len ~ U[128, 512], scale 1/8",
+        4: "long-context: B=1 H=16 N=16384 d=128 bf16 causal, scale 1/sqrt(128)",
+        5: "block-sparse: B=1 H=8 N=65536 d=64 bf16, 128x128 cell mask (band, 2 random cells per row, "
+           "first column), scale 1/8",
+        6: "long-context, head dim 256: B=1 H=8 N=16384 d=256 bf16 causal, scale 1/16",
+        7: "long-context, head dim 96: B=1 H=16 N=16384 d=96 bf16 causal, scale 1/sqrt(96)",
+        8: "long-context, head dim 160: B=1 H=16 N=16384 d=160 bf16 causal, scale 1/sqrt(160)"}
+
 
 def copy_calibration():
     """One device-to-device copy of COPY_BYTES: read COPY_BYTES, write COPY_BYTES.
@@ -372,9 +395,21 @@ def cpu_baseline(w, inp, heads=6):
 
 
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "long_context_hbm_traffic.txt")
-KERNEL_SYMBOL = {"fwd": "fwd_bf16_kernel<128, 0>", "dkdv": "dkdv_bf16_kernel<128, 0, false>",
-                 "dq": "dq_bf16_kernel<128, 0>", "pre": "bwd_pre_kernel"}
+# Counter summaries per workload, and the kernels each stage of a step launches
+# (a stage's bytes are the sum over its kernels; the block-mask dK/dV stage
+# also runs the split count and plan kernels).
+TRAFFIC_FILES = {2: "gpt2_shaped_hbm_traffic.txt", 3: "bert_shaped_hbm_traffic.txt",
+                 4: "long_context_hbm_traffic.txt", 5: "block_sparse_hbm_traffic.txt"}
+TRAFFIC_FILE = os.path.join(PROFILES, TRAFFIC_FILES[4])
+
+
+def stage_symbols(d, block_mask):
+    split = "true" if block_mask else "false"
+    return {"fwd": [f"fwd_bf16_kernel<{d}, 0>"],
+            "pre": ["bwd_pre_kernel"],
+            "dkdv": [f"dkdv_bf16_kernel<{d}, 0, {split}>"] + (["split_count_kernel", "split_plan_kernel"]
+                                                               if block_mask else []),
+            "dq": [f"dq_bf16_kernel<{d}, 0>"]}
 
 
 def kernel_source_hash():
@@ -388,13 +423,14 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per launch from the committed counter summary, or {} when the
-    kernels changed after the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(workload=4):
+    """HBM bytes per launch from the committed counter summary of a workload,
+    or {} when there is none or the kernels changed after it was taken."""
+    path = os.path.join(PROFILES, TRAFFIC_FILES.get(workload, "-"))
+    if not os.path.exists(path):
         return {}
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if "=" in line and not line.startswith("#"):
             k, v = line.strip().split("=", 1)
             kv[k.strip()] = v.strip()
@@ -403,12 +439,16 @@ def read_traffic():
     return {k[len("bytes_"):]: float(v) for k, v in kv.items() if k.startswith("bytes_")}
 
 
-def summarize_counters(fetch_csv, write_csv, command):
-    """Write the per-kernel HBM traffic summary from two rocprofv3 --pmc runs
-    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch).  Each counter is scaled by its
-    reading for the plain copy of COPY_BYTES made by --copy-calibration."""
+def summarize_counters(fetch_csv, write_csv, command, workload=4):
+    """Write a workload's per-kernel HBM traffic summary from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch).  Each counter is scaled by
+    its reading for the plain copy of COPY_BYTES made by --copy-calibration."""
     import csv
     import statistics
+
+    from workloads import WORKLOADS
+    w = WORKLOADS[workload]
+    symbols = stage_symbols(w.d, workload == 5)
 
     def per_kernel(path, counter):
         vals = {}
@@ -421,37 +461,52 @@ def summarize_counters(fetch_csv, write_csv, command):
     copy_name = next(n for n in fetch if "copyBuffer" in n)
     f_scale = (COPY_BYTES / 1024) / max(fetch[copy_name])
     w_scale = (COPY_BYTES / 1024) / max(write[copy_name])
-    lines = ["# HBM traffic per launch, long-context workload (B=1 H=16 N=16384 d=128 bf16 causal)",
+    lines = [f"# HBM traffic per launch, {DESC[workload]}",
              f"# command: {command}",
              f"# calibration: a {COPY_BYTES >> 20} MiB device copy reads FETCH_SIZE {max(fetch[copy_name]):.1f} KiB "
              f"(scale {f_scale:.4f}) and WRITE_SIZE {max(write[copy_name]):.1f} KiB (scale {w_scale:.4f})",
              f"source_hash = {kernel_source_hash()}",
              f"fetch_scale = {f_scale:.6f}", f"write_scale = {w_scale:.6f}"]
-    for key, sym in KERNEL_SYMBOL.items():
-        fn = [n for n in fetch if sym in n or (key == "pre" and "bwd_pre" in n)]
-        wn = [n for n in write if sym in n or (key == "pre" and "bwd_pre" in n)]
-        if not fn or not wn:
-            raise SystemExit(f"no {key} kernel ({sym}) in the counter files; kernel names: {sorted(fetch)}")
-        fb = statistics.median(fetch[fn[0]]) * 1024 * f_scale
-        wb = statistics.median(write[wn[0]]) * 1024 * w_scale
+    for key, syms in symbols.items():
+        fb = wb = 0.0
+        for sym in syms:
+            fn = [n for n in fetch if sym in n]
+            wn = [n for n in write if sym in n]
+            if len(fn) != 1 or len(wn) != 1:
+                raise SystemExit(f"{key}: kernel {sym} matches {fn} in the counter files; names: {sorted(fetch)}")
+            fb += statistics.median(fetch[fn[0]]) * 1024 * f_scale
+            wb += statistics.median(write[wn[0]]) * 1024 * w_scale
         lines += [f"fetch_{key} = {fb:.0f}", f"write_{key} = {wb:.0f}", f"bytes_{key} = {fb + wb:.0f}"]
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(os.path.join(PROFILES, TRAFFIC_FILES[workload]), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def kernel_table(w, per, f_fwd, B, H, N, d):
-    """Per-kernel achieved TFLOP/s and compulsory-traffic GB/s, and the bound
-    implied by arithmetic intensity (flops per compulsory byte) against the
-    ridge point peak_flops / peak_bandwidth."""
+def kernel_table(w, per, f_fwd, B, H, N, d, samples=None, traffic=None):
+    """Per-kernel achieved TFLOP/s (executed products; for dQ also its one
+    algorithmic product), compulsory-traffic GB/s ("alg_gbs"), the bound implied
+    by arithmetic intensity (flops per compulsory byte) against the ridge point
+    peak_flops / peak_bandwidth, and, with a matching counter summary, the
+    measured HBM bytes and GB/s."""
+    import statistics
     esize = 2 if w.dtype == "bf16" else 4
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     out = {}
     for n, ms in per.items():
         fl, by = kernel_flops(n, f_fwd), kernel_bytes(n, B, H, N, d, esize)
-        out[n] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
-                  "hbm_gbs": round(by / (ms * 1e-3) / 1e9, 1), "alg_bytes": by,
-                  "bound": "mfma" if fl / by > ridge else "hbm"}
+        row = {"ms": round(ms, 4)}
+        if samples:
+            row["ms_median"] = round(statistics.median(samples[n]), 4)
+            row["ms_min"] = round(min(samples[n]), 4)
+        row.update({"tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                    "alg_gbs": round(by / (ms * 1e-3) / 1e9, 1), "alg_bytes": by,
+                    "bound": "mfma" if fl / by > ridge else "hbm"})
+        if ALG_PRODUCTS[n] != PRODUCTS[n]:
+            row["alg_tflops"] = round(ALG_PRODUCTS[n] * f_fwd / 2 / (ms * 1e-3) / 1e12, 2)
+        if traffic and n in traffic:
+            row["hbm_bytes"] = traffic[n]
+            row["hbm_gbs"] = round(traffic[n] / (ms * 1e-3) / 1e9, 1)
+        out[n] = row
     return out
 
 
@@ -470,7 +525,7 @@ def sweep(steps, warmup):
             inp = {n: a.reshape(B, 16, N, d) for n, a in zip(("q", "k", "v", "do"), flat)}
             for causal in (False, True):
                 w = Workload(0, "sweep", B, 16, N, d, "bf16", causal, 1.0 / math.sqrt(d), 1.0)
-                step_ms, per, _, _ = run_gpu_bench(w, steps, warmup, inp)
+                step_ms, per, _, _, _ = run_gpu_bench(w, steps, warmup, inp)
                 F = workload_fwd_flops(w, inp)
                 t_bwd = per["pre"] + per["dkdv"] + per["dq"]
                 line = {"B": B, "H": 16, "N": N, "d": d, "causal": causal, "ms_per_step": round(step_ms, 4),
@@ -499,11 +554,14 @@ def main():
     ap.add_argument("--cpu-baseline", action="store_true", help="run the CPU oracle leg for --workload other than 4")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, run one plain device copy of COPY_BYTES (counter calibration)")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MiB scrub buffer before every timed launch (cold L2 and MALL)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
-                    help="write profiles/long_context_hbm_traffic.txt from two rocprofv3 --pmc runs and exit")
+                    help="write the --workload's HBM traffic summary under profiles/ from two rocprofv3 --pmc runs "
+                         "and exit")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, workload=args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the attention hot path here is "
@@ -556,10 +614,11 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration()
-    step_ms, per, wall, (B, H, N, d) = run_gpu_bench(w, args.steps, args.warmup, inp)
+    step_ms, per, wall, (B, H, N, d), samples = run_gpu_bench(w, args.steps, args.warmup, inp, cold=args.cold)
     F = workload_fwd_flops(w, inp)
     value = 3.5 * F / (step_ms * 1e-3) / 1e12
-    table = kernel_table(w, per, F, B, H, N, d)
+    traffic = {} if args.cold else read_traffic(args.workload)
+    table = kernel_table(w, per, F, B, H, N, d, samples, traffic)
 
     dom = max(("fwd", "dkdv", "dq"), key=lambda n: per[n])
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -568,22 +627,14 @@ def main():
         roofline = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": peak, "unit": "TFLOP/s",
                     "frac": round(ach / peak, 4)}
     else:
-        ach = table[dom]["hbm_gbs"]
+        ach = table[dom]["alg_gbs"]
         roofline = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(ach / PEAK_HBM_GBS, 4)}
-    traffic = read_traffic() if args.workload == 4 else {}
     roofline["traffic"] = traffic.get(dom)
-    desc = {1: "tiny exact: B=1 H=2 N=128 d=64 fp32, scale 1/8",
-            2: "GPT-2 shaped: B=8 H=12 N=1024 d=64 bf16 causal, scale 1/8",
-            3: "BERT-large shaped: B=32 H=16 N=512 d=64 bf16, key padding kv_len ~ U[128, 512], scale 1/8",
-            4: "long-context: B=1 H=16 N=16384 d=128 bf16 causal, scale 1/sqrt(128)",
-            6: "long-context, head dim 256: B=1 H=8 N=16384 d=256 bf16 causal, scale 1/16",
-            7: "long-context, head dim 96: B=1 H=16 N=16384 d=96 bf16 causal, scale 1/sqrt(96)",
-            8: "long-context, head dim 160: B=1 H=16 N=16384 d=160 bf16 causal, scale 1/sqrt(160)",
-            5: "block-sparse: B=1 H=8 N=65536 d=64 bf16, 128x128 cell mask (band, 2 random cells per row, "
-               "first column), scale 1/8"}[args.workload]
-    config = {"workload": desc, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+    config = {"workload": DESC[args.workload], "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
               "input_sha256": digest(inp["q"], inp["k"], inp["v"])}
+    if args.cold:
+        config["cold"] = "512 MiB scrub before every launch; step = sum of kernel times"
     if inp.get("block_mask") is not None:
         config["mask_cells"] = int(inp["block_mask"].sum())
     out = {

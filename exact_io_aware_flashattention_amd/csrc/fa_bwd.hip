@@ -133,17 +133,6 @@ __device__ __forceinline__ void mma_from_transposed(f32x16& acc, const T* tr, in
   for (int g = 0; g < 4; ++g) q[g].load(row + 8 * g);
   mma_acc_operand(acc, q, x);
 }
-template <int D>
-__device__ __forceinline__ void mma_from_transposed_packed(f32x16& acc, const bf16* tr, int nb, int half,
-                                                           const PackedB& x) {
-  using TL = Tile64<bf16, D>;
-  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
-  Quad<bf16> q[4];
-  const bf16* row = tr + (32 * nb + l32) * TL::TP + 32 * half + 4 * h;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) q[g].load(row + 8 * g);
-  mma_packed(acc, q, x);
-}
 
 template <typename T, int D>
 __device__ __forceinline__ void store_acc_rows(T* base, int row, int N, const f32x16 (&acc)[D / 32], float mul) {
@@ -309,19 +298,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DkdvCfg<T, D
             }
           }
           // dV^T += dO^T P,  dK^T += Q^T dS
-          if constexpr (sizeof(T) == 2) {
-            const PackedB pb = pack_bf16(s), db = pack_bf16(dp);
 #pragma unroll
-            for (int nb = 0; nb < TL::NB; ++nb) {
-              mma_from_transposed_packed<D>(dv[nb], dOt, nb, qs, pb);
-              mma_from_transposed_packed<D>(dk[nb], Qt, nb, qs, db);
-            }
-          } else {
-#pragma unroll
-            for (int nb = 0; nb < TL::NB; ++nb) {
-              mma_from_transposed<T, D>(dv[nb], dOt, nb, qs, s);
-              mma_from_transposed<T, D>(dk[nb], Qt, nb, qs, dp);
-            }
+          for (int nb = 0; nb < TL::NB; ++nb) {
+            mma_from_transposed<T, D>(dv[nb], dOt, nb, qs, s);
+            mma_from_transposed<T, D>(dk[nb], Qt, nb, qs, dp);
           }
         }
       }
@@ -461,14 +441,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occ<T>::W, O
             dp[r] = p * (dp[r] - del);
           }
           // dQ^T += K^T dS^T
-          if constexpr (sizeof(T) == 2) {
-            const PackedB db = pack_bf16(dp);
 #pragma unroll
-            for (int nb = 0; nb < TL::NB; ++nb) mma_from_transposed_packed<D>(dq[nb], Kt, nb, sb, db);
-          } else {
-#pragma unroll
-            for (int nb = 0; nb < TL::NB; ++nb) mma_from_transposed<T, D>(dq[nb], Kt, nb, sb, dp);
-          }
+          for (int nb = 0; nb < TL::NB; ++nb) mma_from_transposed<T, D>(dq[nb], Kt, nb, sb, dp);
         }
       }
       if (CF::NSTAGE == 1) __syncthreads();

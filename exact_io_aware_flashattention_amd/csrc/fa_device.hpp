@@ -35,7 +35,8 @@ constexpr int MAX_T = 2048;    // largest number of mask cells per side
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float TAU = 8.0f;    // the running max is refreshed only when a tile
-                               // exceeds it by more than 2^TAU (see softmax_update)
+                               // exceeds it by more than 2^TAU (the refresh step of
+                               // the bf16 forward, fa_bf16.hip)
 
 // Waves per SIMD the bf16 kernels are register-limited to: two resident waves
 // let one wave's softmax VALU work overlap the other's matrix-core work.
@@ -119,17 +120,7 @@ __device__ __forceinline__ void mma_chunk(f32x16& acc, u32x4 a, u32x4 b, float*)
 // B-side values sit in the accumulator layout `x` of a previous product
 // (register r <-> contraction index 8*(r/4) + 4*h + r%4).  a[g] holds the
 // 4 A-side elements for contraction indices 8*g + 4*h + 0..3 of this lane's
-// A row.
-__device__ __forceinline__ void mma_acc_operand(f32x16& acc, const Quad<bf16> (&a)[4], const f32x16& x) {
-#pragma unroll
-  for (int mm = 0; mm < 2; ++mm) {
-    u32x4 av = {a[2 * mm].v[0], a[2 * mm].v[1], a[2 * mm + 1].v[0], a[2 * mm + 1].v[1]};
-    bf16x8 bv;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) bv[j] = (bf16)x[8 * mm + j];
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bv, acc, 0, 0, 0);
-  }
-}
+// A row (fp32 path).
 __device__ __forceinline__ void mma_acc_operand(f32x16& acc, const Quad<float> (&a)[4], const f32x16& x) {
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -139,8 +130,8 @@ __device__ __forceinline__ void mma_acc_operand(f32x16& acc, const Quad<float> (
   }
 }
 
-// Same with the B-side values already converted (bf16 pairs packed per
-// register pair, see pack_bf16).
+// Accumulator-layout values (probabilities, dS) rounded to bf16 and packed as
+// the two 8-element B operands of a 32x32x16 product over their 32 indices.
 struct PackedB { bf16x8 p[2]; };
 __device__ __forceinline__ PackedB pack_bf16(const f32x16& x) {
   PackedB r;
@@ -149,13 +140,6 @@ __device__ __forceinline__ PackedB pack_bf16(const f32x16& x) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) r.p[mm][j] = (bf16)x[8 * mm + j];
   return r;
-}
-__device__ __forceinline__ void mma_packed(f32x16& acc, const Quad<bf16> (&a)[4], const PackedB& b) {
-#pragma unroll
-  for (int mm = 0; mm < 2; ++mm) {
-    u32x4 av = {a[2 * mm].v[0], a[2 * mm].v[1], a[2 * mm + 1].v[0], a[2 * mm + 1].v[1]};
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), b.p[mm], acc, 0, 0, 0);
-  }
 }
 
 // ---------------------------------------------------------------- cross-lane

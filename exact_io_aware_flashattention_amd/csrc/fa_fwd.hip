@@ -202,25 +202,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Occ<T>::W, O
         // step 4: O^T += V^T P~^T
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-          if constexpr (sizeof(T) == 2) {
-            const PackedB pb = pack_bf16(s[sb]);
 #pragma unroll
-            for (int nb = 0; nb < TL::NB; ++nb) {
-              Quad<T> vq[4];
-              const T* vrow = Vt + (32 * nb + l32) * TL::VP + 32 * sb + 4 * h;
+          for (int nb = 0; nb < TL::NB; ++nb) {
+            Quad<T> vq[4];
+            const T* vrow = Vt + (32 * nb + l32) * TL::VP + 32 * sb + 4 * h;
 #pragma unroll
-              for (int g = 0; g < 4; ++g) vq[g].load(vrow + 8 * g);
-              mma_packed(acc[nb], vq, pb);
-            }
-          } else {
-#pragma unroll
-            for (int nb = 0; nb < TL::NB; ++nb) {
-              Quad<T> vq[4];
-              const T* vrow = Vt + (32 * nb + l32) * TL::VP + 32 * sb + 4 * h;
-#pragma unroll
-              for (int g = 0; g < 4; ++g) vq[g].load(vrow + 8 * g);
-              mma_acc_operand(acc[nb], vq, s[sb]);
-            }
+            for (int g = 0; g < 4; ++g) vq[g].load(vrow + 8 * g);
+            mma_acc_operand(acc[nb], vq, s[sb]);
           }
         }
       }

@@ -3,12 +3,14 @@ library through its C ABI binding, and compare against the fp64 oracle.
 
 Tolerances (stated for the hot path of exact attention):
   float32 inputs: max |dO| <= 1e-5, max |dlse| <= 1e-5, gradients max|d|/max|g| <= 1e-5
-  bf16 inputs:    |dO| <= 1e-2 max(1, |O|) per element and mean |dO| <= 1e-3,
+  bf16 inputs:    |dO| <= 1e-2 max(1, |O|) per element (and <= 1e-2 wherever
+                  |O| < 2), mean |dO| <= 1e-3,
                   max |dlse| <= 1e-3, gradients max|d| / max|g_oracle| <= 5e-2 per tensor
 The bf16 bound on O is the stated 1e-2 for outputs of magnitude up to 1 and 1 %
 relative above: a row with one or two allowed keys has |O| up to |V| (about 3-4
 for normal inputs), where rounding the output to bf16 alone moves it by up to
-2^-9 |O| and the bf16 probabilities of the P V product by up to 2^-9 |V|.
+2^-8 |O| (bf16's unit roundoff: 0.0129 at |O| = 3.3, above 1e-2) and the bf16
+probabilities of the P V product by up to 2^-8 |V|.
 """
 import sys
 
@@ -70,6 +72,13 @@ def compare_forward(o, lse, o_ref, lse_ref, dtype, what=""):
         lim = tol["o_max"] * np.maximum(1.0, np.abs(o_ref))
         bad = d > lim
         assert not bad.any(), f"{what}: |dO| {d[bad].max():.3e} above 1e-2 max(1, |O|) at {np.argwhere(bad)[:3]}"
+        # the stated absolute bound wherever bf16 output rounding allows it
+        # (|O| < 2: the output's own rounding is at most 2^-8)
+        small = np.abs(o_ref) < 2.0
+        if small.any():
+            assert d[small].max() <= tol["o_max"], f"{what}: |dO| {d[small].max():.3e} > 1e-2 where |O| < 2"
+        over = int((d > tol["o_max"]).sum())
+        say(f"  {what} elements with |dO| > 1e-2 (all at |O| >= 2): {over} of {d.size}")
     else:
         assert d.max() <= tol["o_max"], f"{what}: max|dO| {d.max():.3e}"
     assert d.mean() <= tol["o_mean"], f"{what}: mean|dO| {d.mean():.3e}"

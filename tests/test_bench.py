@@ -87,5 +87,21 @@ def test_profiled_kernel_names_exist_in_the_library():
     if not os.path.exists(lib) or shutil.which("nm") is None:
         pytest.skip("libfa.so not built or nm not available")
     syms = subprocess.run(["nm", "-C", lib], stdout=subprocess.PIPE, text=True, check=True).stdout
-    for key, sym in bench.KERNEL_SYMBOL.items():
-        assert sym in syms, f"{key}: no kernel named {sym} in libfa.so"
+    for wl in bench.TRAFFIC_FILES:
+        w = WORKLOADS[wl]
+        for key, names in bench.stage_symbols(w.d, wl == 5).items():
+            for sym in names:
+                assert sym in syms, f"workload {wl} {key}: no kernel named {sym} in libfa.so"
+
+
+def test_kernel_table_reports_median_min_and_measured_traffic():
+    w = WORKLOADS[4]
+    f = bench.workload_fwd_flops(w, {})
+    per = {"fwd": 1.0, "pre": 0.02, "dkdv": 2.0, "dq": 1.5}
+    samples = {"fwd": [0.9, 1.0, 1.1], "pre": [0.02] * 3, "dkdv": [2.0, 1.9, 2.1], "dq": [1.5, 1.6, 1.4]}
+    table = bench.kernel_table(w, per, f, 1, 16, 16384, 128, samples, {"fwd": 8e8})
+    assert table["fwd"]["ms_median"] == 1.0 and table["fwd"]["ms_min"] == 0.9
+    assert math.isclose(table["fwd"]["hbm_gbs"], 8e8 / 1e-3 / 1e9, rel_tol=1e-3)
+    assert "hbm_gbs" not in table["dq"]
+    # dQ owes one product; it executes three (S and dP recomputed)
+    assert math.isclose(table["dq"]["alg_tflops"] * 3, table["dq"]["tflops"], rel_tol=1e-3)
