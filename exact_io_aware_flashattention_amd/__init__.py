@@ -23,7 +23,7 @@ CELL = 128
 
 EXPORTS = ("fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd_dkdv_workspace_bytes", "fa_bwd", "fa_bwd_preprocess",
            "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_splitkv_workspace_bytes",
-           "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv", "fa_fwd_splitkv_fp8kv", "fa_fwd_fp8", "fa_debug_visits", "fa_status_str")
+           "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_fwd_splitkv_fp8kv", "fa_fwd_fp8", "fa_debug_visits", "fa_status_str")
 
 
 class FAError(RuntimeError):
@@ -62,6 +62,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fa_fwd_splitkv_workspace_bytes": [I, I, I, I, I, I],
         "fa_fwd_splitkv_num_splits": [I, I, I, I, I],
         "fa_fwd_splitkv": [P, P, P, P, P, I, I, I, I, I, F, I, P, I, I, P, S, P],
+        "fa_fwd_splitkv_noalloc": [P, P, P, P, P, I, I, I, I, I, F, I, P, I, I, P],
         "fa_fwd_fp8": [P, P, P, P, P, I, I, I, I, F, I, P, P, F, F, F, P],
         "fa_fwd_splitkv_fp8kv": [P, P, P, P, P, I, I, I, I, I, F, I, P, F, F, I, P, S, P],
         "fa_debug_visits": [I, I, I, I, I, I, P, P, I, P, P, S, P],
@@ -208,6 +209,23 @@ def fa_fwd(q, k, v, o=None, lse=None, *, scale=None, causal=False, block_mask=No
     else:
         _call("fa_fwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _scale(scale, d),
               int(bool(causal)), mb, kl, _dtype_code(q), _stream(stream))
+    return o, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20     # FA_NOALLOC_SCRATCH_BYTES of include/fa.h
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, *, scale=None, causal=False, kv_len=None, num_splits=0, stream=None):
+    """fa_fwd_splitkv into caller-provided o and lse, with the partial results in
+    the library's fixed per-GPU scratch instead of a workspace (for callers
+    that cannot allocate; nothing is allocated here either)."""
+    import torch
+    if o is None or lse is None:
+        raise ValueError("fa_fwd_splitkv_noalloc writes into caller-provided o and lse")
+    B, H, Nq, Nk, d = _check_split(q, k, v, o, lse, kv_len, torch.bfloat16, None)
+    _call("fa_fwd_splitkv_noalloc", _ptr(q), _ptr(k) if Nk else None, _ptr(v) if Nk else None, _ptr(o), _ptr(lse),
+          B, H, Nq, Nk, d, _scale(scale, d), int(bool(causal)), _ptr(kv_len), _dtype_code(q), int(num_splits),
+          _stream(stream))
     return o, lse
 
 

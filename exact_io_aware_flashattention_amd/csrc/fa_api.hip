@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_kernels.hpp"
@@ -315,6 +316,38 @@ size_t splitkv_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
   return splitkv_o_bytes(B, H, Nq, d, p.nsplit) + (size_t)p.nsplit * B * H * Nq * 2 * sizeof(float);
 }
 
+// ---------------------------------------------------------------- fixed scratch
+
+// Device buffer of fa_fwd_splitkv_noalloc, for callers that cannot allocate:
+// one per GPU (the code object is loaded on every device the library runs
+// on), held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not the device memory: its device address is looked up once per
+// device with hipGetSymbolAddress, and only that address is passed to kernels.
+__device__ __attribute__((aligned(256))) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (the first call on a
+// device looks it up with that device current).
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+int splitkv_run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                int d, float scale, int causal, const int32_t* kv_len, int dtype, int num_splits, void* workspace,
+                size_t workspace_bytes, void* stream, bool use_scratch);
+
 }  // namespace
 
 extern "C" {
@@ -328,6 +361,8 @@ const char* fa_status_str(int status) {
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not suitably aligned";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP launch failed";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the sizes need more than the library's fixed scratch (FA_NOALLOC_SCRATCH_BYTES)";
     case FA_ERR_ARG: return "FA_ERR_ARG: invalid scale or selector";
     default: return "unknown fa status";
   }
@@ -407,6 +442,26 @@ int fa_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int num_splits) {
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
                    int d, float scale, int causal, const int32_t* kv_len, int dtype, int num_splits,
                    void* workspace, size_t workspace_bytes, void* stream) {
+  return splitkv_run(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_len, dtype, num_splits, workspace,
+                     workspace_bytes, stream, false);
+}
+
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                           int Nk, int d, float scale, int causal, const int32_t* kv_len, int dtype, int num_splits,
+                           void* stream) {
+  return splitkv_run(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, kv_len, dtype, num_splits, nullptr, 0,
+                     stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// fa_fwd_splitkv with the caller's workspace, or (use_scratch) with the
+// library's fixed scratch of the current device; every check runs first.
+int splitkv_run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                int d, float scale, int causal, const int32_t* kv_len, int dtype, int num_splits, void* workspace,
+                size_t workspace_bytes, void* stream, bool use_scratch) {
   bool empty = false;
   FA_TRY(check_splitkv_shape(B, H, Nq, Nk, d, dtype, &empty));
   if (empty) return FA_OK;
@@ -417,9 +472,15 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   FA_TRY(check_rowstats({lse}));
   FA_TRY(check_masks(nullptr, kv_len));
   FA_TRY(check_scale(scale));
-  if (!workspace) return FA_ERR_NULL;
-  if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
-  if (workspace_bytes < splitkv_bytes(B, H, Nq, Nk, d, num_splits)) return FA_ERR_WORKSPACE;
+  const size_t need = splitkv_bytes(B, H, Nq, Nk, d, num_splits);
+  if (use_scratch) {
+    if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+    FA_TRY(scratch_on_current_device(&workspace));
+  } else {
+    if (!workspace) return FA_ERR_NULL;
+    if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+    if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  }
   fa::AttnArgs a = make_args(Shape{B, H, Nq, d, dtype}, scale, causal, nullptr, kv_len);
   a.q = q;
   a.k = k;
@@ -436,6 +497,10 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(p.decode ? fa::launch_fwd_decode_bf16(a, d, st) : fa::launch_fwd_splitkv_bf16(a, d, st));
 }
+
+}  // namespace
+
+extern "C" {
 
 int fa_fwd_splitkv_fp8kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
                          int Nk, int d, float scale, int causal, const int32_t* kv_len, float k_descale,

@@ -76,8 +76,13 @@ enum fa_status {
   FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE = 5, /* workspace smaller than the matching *_workspace_bytes() */
   FA_ERR_HIP = 6,       /* a HIP launch failed */
-  FA_ERR_ARG = 7        /* scale not finite and > 0, bad selector, or bad dropout rate */
+  FA_ERR_ARG = 7,       /* scale not finite and > 0, bad selector, or bad dropout rate */
+  FA_ERR_SCRATCH = 8    /* fa_fwd_splitkv_noalloc: sizes need more than FA_NOALLOC_SCRATCH_BYTES */
 };
+
+/* Size of the fixed device scratch behind fa_fwd_splitkv_noalloc (64 MiB per
+ * GPU the library runs on). */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /*
  * Forward pass.  Writes o [B,H,N,d] (dtype) and lse [B,H,N] (float32), with
@@ -248,6 +253,25 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int Nq, int Nk, int d, float scale, int causal,
                    const int32_t* kv_len, int dtype, int num_splits,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_splitkv without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The partial results go to a fixed
+ * device buffer of FA_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends; the call itself allocates nothing.
+ * Arguments, results and errors are those of fa_fwd_splitkv (the same kernels
+ * and range plan, so the outputs are bit-identical), plus FA_ERR_SCRATCH when
+ * fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits) exceeds
+ * FA_NOALLOC_SCRATCH_BYTES (checked before anything is launched; an explicit
+ * smaller num_splits needs less).  The stream must belong to the current
+ * device, whose buffer is used.  Every call on one GPU shares that GPU's
+ * buffer, which keeps the last call's contents (nothing in it needs to start
+ * at zero): calls that overlap in time on one GPU race.
+ */
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                           const int32_t* kv_len, int dtype, int num_splits, void* stream);
 
 /*
  * Decoding against an 8-bit key/value cache: fa_fwd_splitkv for Nq <= 4 bf16

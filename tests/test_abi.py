@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         assert fa.fa_status_str(s).startswith("FA_")
     assert "unknown" in fa.fa_status_str(99)
 
@@ -227,3 +227,23 @@ def test_library_links_only_hip_runtime():
     needed = re.findall(r"\[(.*?)\]", "\n".join(l for l in out.splitlines() if "NEEDED" in l))
     assert any("amdhip64" in n for n in needed)
     assert not any("torch" in n or "python" in n for n in needed)
+
+
+def test_noalloc_splitkv_validation(lib):
+    """fa_fwd_splitkv_noalloc checks its arguments like fa_fwd_splitkv and
+    refuses, before anything is launched, sizes whose partial results would
+    not fit the fixed scratch (64 MiB)."""
+    P = FAKE
+    assert fa.NOALLOC_SCRATCH_BYTES == 64 << 20
+    text = open(HEADER).read()
+    assert "#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+
+    def call(B=1, H=2, Nq=10, Nk=500, d=128, dtype=0, ns=0, scale=0.1, k=P, q=P):
+        return lib.fa_fwd_splitkv_noalloc(q, k, P, P, P, B, H, Nq, Nk, d, scale, 1, None, dtype, ns, None)
+    big = dict(B=8, H=16, Nq=4096, Nk=16384, d=128, ns=2)
+    assert lib.fa_fwd_splitkv_workspace_bytes(8, 16, 4096, 16384, 128, 2) > fa.NOALLOC_SCRATCH_BYTES
+    assert call(**big) == 8
+    assert "FA_ERR_SCRATCH" in fa.fa_status_str(8)
+    assert call(dtype=1) == 3 and call(d=80) == 2 and call(ns=1025) == 7 and call(scale=0.0) == 7
+    assert call(k=None) == 1 and call(q=P + 8) == 4
+    assert call(Nq=0) == 0                  # nothing to compute
