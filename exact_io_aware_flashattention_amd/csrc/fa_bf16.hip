@@ -257,14 +257,52 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC
 
     // One 64-key tile j held in LDS stage STG: sub-blocks 2j (in sa) and 2j+1.
     f32x16 sa, sb;
-    auto tile_step = [&](auto stg, int j) {
-      constexpr int STG = decltype(stg)::value;
-      using S0 = std::integral_constant<int, STG>;
-      using S1 = std::integral_constant<int, 1 - STG>;
+    auto tile_begin = [&](int j) {
       if (j > 0) wait_loads();     // K of tile j+1 and V of tile j, issued one tile ago
       __syncthreads();
       if (j + 2 < ntiles) issue_k(j + 2);
       if (j + 1 < ntiles) issue_v(j + 1);
+    };
+    // Sub-block t needs no mask: it exists and every key of it is below
+    // kv_len and (causal) at or before every query of this wave.  Along a
+    // walk the keys only grow, so the sub-blocks that need no mask are a
+    // prefix of it.
+    auto clean = [&](int t) -> bool {
+      if (t >= nsub) return false;
+      const int k0 = key0(t);
+      return k0 + 32 <= kvl && (!a.causal || k0 + 31 <= qw0 + off);
+    };
+    // Tile step whose scores S(2j+1) and S(2j+2) need no mask (every tile but
+    // the last one or two of a walk): each sub-block -- scores of the next
+    // sub-block, softmax and P V of this one, row sum and max of the next --
+    // is one branch-free region closed by the refresh test, so the row sum
+    // and the max overlap the P V products.
+    auto interior_step = [&](auto stg, int j) {
+      constexpr int STG = decltype(stg)::value;
+      using S0 = std::integral_constant<int, STG>;
+      using S1 = std::integral_constant<int, 1 - STG>;
+      tile_begin(j);
+      if (!live) return;
+      read_v(S0(), I0());
+      scores(sb);
+      softmax_pv(sa, 2 * j);
+      read_k(S1(), I0());
+      const float mx1 = max16(sb);
+      interleave_mfma_valu();
+      refresh(mx1);
+      read_v(S0(), I1());
+      scores(sa);
+      softmax_pv(sb, 2 * j + 1);
+      read_k(S1(), I1());
+      const float mx2 = max16(sa);
+      interleave_mfma_valu();
+      refresh(mx2);
+    };
+    auto tile_step = [&](auto stg, int j) {
+      constexpr int STG = decltype(stg)::value;
+      using S0 = std::integral_constant<int, STG>;
+      using S1 = std::integral_constant<int, 1 - STG>;
+      tile_begin(j);
       if (!live) return;
       // sub-block 2j: S(2j+1) while softmax(2j); then O += P~ V
       read_v(S0(), I0());
@@ -294,7 +332,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC
         read_k(I0(), I1());
         refresh(mask_max(sa, 0));
       }
-      for (int j = 0; j < ntiles; j += 2) {
+      // steps j and j + 1 are interior iff sub-block 2j + 4 needs no mask
+      int j = 0;
+      for (; clean(2 * j + 4); j += 2) {
+        interior_step(I0(), j);
+        interior_step(I1(), j + 1);
+      }
+      for (; j < ntiles; j += 2) {
         tile_step(I0(), j);
         if (j + 1 < ntiles) tile_step(I1(), j + 1);
       }
