@@ -174,9 +174,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC
     auto read_v = [&](auto stage, auto half) {
       const unsigned char* vs = vbuf + decltype(stage)::value * C::TILE;
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
+      for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm)
+        for (int nb = 0; nb < C::NB; ++nb)
           vfrag[nb][mm] = tr_operand<D>(vs, 32 * decltype(half)::value + 16 * mm, 32 * nb);
     };
     auto scores = [&](f32x16& s) {
@@ -246,11 +246,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC
         for (int r = 0; r < 16; ++r)
           if (!keep_byte(keepw[r >> 2], r & 3, a.drop_t)) s[r] = 0.f;
       }
+      // keys 0-15 of the sub-block first, so the exponentials of keys 16-31
+      // can overlap the first half of the products
       const PackedB pb = pack_bf16(s);
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
+      for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) mma(acc[nb], vfrag[nb][mm], pb.p[mm]);
+        for (int nb = 0; nb < C::NB; ++nb) mma(acc[nb], vfrag[nb][mm], pb.p[mm]);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
