@@ -69,9 +69,11 @@ struct FwdB {
   static constexpr int TILE = BC * BTile<D>::ROWB;   // LDS bytes of one K or V tile
   static constexpr int SSTEPS = D / 16;
   static constexpr int NB = D / 32;
-  // waves per SIMD: two (<= 256 registers) up to d = 128; above, the
+  // waves per SIMD: three at d = 64 (<= 168 registers: the softmax VALU work
+  // of one wave then has two others to overlap, and short walks hide their
+  // start and end), two (<= 256 registers) up to d = 128; above, the
   // accumulation and operand registers need a single wave per SIMD
-  static constexpr int OCC = D > 128 ? 1 : 2;
+  static constexpr int OCC = D > 128 ? 1 : (D == 64 ? 3 : 2);
 };
 
 // Forward, software-pipelined over 32-key sub-blocks t = 0, 1, ... of the walk:
