@@ -1,7 +1,8 @@
 """Benchmark of the attention hot path on one MI355X.
 
-One step = one forward (fa_fwd) and one backward (fa_bwd's three stages:
-delta preprocess, dK/dV, dQ) over the long-context workload: B=1, H=16,
+One step = one forward (fa_fwd) and one backward (fa_bwd's two stages: dQ
+with the row terms delta = rowsum(dO * O) formed in the same kernel, then
+dK/dV) over the long-context workload: B=1, H=16,
 N=16384, d=128, bf16, causal, scale 1/sqrt(128), Q/K/V/dO ~ N(0, 0.5) from the
 seeded generator.  Inputs are resident in HBM before timing starts.
 
@@ -84,10 +85,10 @@ def workload_fwd_flops(w, inp):
     return f
 
 
-PRODUCTS = {"fwd": 2, "dkdv": 4, "dq": 3, "pre": 0}
+PRODUCTS = {"fwd": 2, "dkdv": 4, "dq": 3}
 # Products each kernel owes the method (dQ = scale dS K is one product; S and
 # dP are recomputed in the dQ kernel, which the executed count includes).
-ALG_PRODUCTS = {"fwd": 2, "dkdv": 4, "dq": 1, "pre": 0}
+ALG_PRODUCTS = {"fwd": 2, "dkdv": 4, "dq": 1}
 
 
 def kernel_flops(name, f_fwd):
@@ -98,10 +99,10 @@ def kernel_flops(name, f_fwd):
 
 def kernel_bytes(name, B, H, N, d, esize):
     """Compulsory HBM bytes per launch (each operand read once, each output
-    written once): the IO lower bound of the pages' complexity analysis."""
+    written once): the IO lower bound of the pages' complexity analysis.  The
+    dQ stage reads Q, K, V, dO, O and lse and writes dQ and delta."""
     t, r = B * H * N * d * esize, B * H * N * 4
-    return {"fwd": 3 * t + t + r, "pre": 2 * t + r, "dkdv": 4 * t + 2 * r + 2 * t,
-            "dq": 4 * t + 2 * r + t}[name]
+    return {"fwd": 3 * t + t + r, "dkdv": 4 * t + 2 * r + 2 * t, "dq": 5 * t + r + t + r}[name]
 
 
 def run_gpu_bench_dropout(w, steps, warmup, inp, p, seed=2024):
@@ -178,9 +179,8 @@ def run_gpu_bench(w, steps, warmup, inp, cold=False):
     stream = torch.cuda.current_stream()
     scrub = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev) if cold else None
     launches = [lambda: fa.fa_fwd(q, k, v, o, lse, stream=stream, **kw),
-                lambda: fa.fa_bwd_preprocess(o, do, delta, stream=stream),
-                lambda: fa.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, workspace=ws, stream=stream, **kw),
-                lambda: fa.fa_bwd_dq(q, k, v, do, lse, delta, dq, stream=stream, **kw)]
+                lambda: fa.fa_bwd_dq_delta(q, k, v, o, do, lse, delta, dq, stream=stream, **kw),
+                lambda: fa.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, workspace=ws, stream=stream, **kw)]
 
     def step(ev=None):
         for j, launch in enumerate(launches):
@@ -195,7 +195,7 @@ def run_gpu_bench(w, steps, warmup, inp, cold=False):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(launches))] for _ in range(steps)]
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -208,7 +208,7 @@ def run_gpu_bench(w, steps, warmup, inp, cold=False):
     _gc_resume()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    names = ["fwd", "pre", "dkdv", "dq"]
+    names = ["fwd", "dq", "dkdv"]
     samples = {n: [ev[2 * j].elapsed_time(ev[2 * j + 1]) for ev in evs] for j, n in enumerate(names)}
     per = {n: sum(s) / steps for n, s in samples.items()}      # mean ms per launch
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(dq).all())
@@ -406,7 +406,6 @@ TRAFFIC_FILE = os.path.join(PROFILES, TRAFFIC_FILES[4])
 def stage_symbols(d, block_mask):
     split = "true" if block_mask else "false"
     return {"fwd": [f"fwd_bf16_kernel<{d}, 0>"],
-            "pre": ["bwd_pre_kernel"],
             "dkdv": [f"dkdv_bf16_kernel<{d}, 0, {split}>"] + (["split_count_kernel", "split_plan_kernel"]
                                                                if block_mask else []),
             "dq": [f"dq_bf16_kernel<{d}, 0>"]}
@@ -527,7 +526,7 @@ def sweep(steps, warmup):
                 w = Workload(0, "sweep", B, 16, N, d, "bf16", causal, 1.0 / math.sqrt(d), 1.0)
                 step_ms, per, _, _, _ = run_gpu_bench(w, steps, warmup, inp)
                 F = workload_fwd_flops(w, inp)
-                t_bwd = per["pre"] + per["dkdv"] + per["dq"]
+                t_bwd = per["dkdv"] + per["dq"]
                 line = {"B": B, "H": 16, "N": N, "d": d, "causal": causal, "ms_per_step": round(step_ms, 4),
                         "fwd_bwd_tflops": round(3.5 * F / (step_ms * 1e-3) / 1e12, 1),
                         "fwd_tflops": round(F / (per["fwd"] * 1e-3) / 1e12, 1),

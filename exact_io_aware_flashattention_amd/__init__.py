@@ -22,7 +22,7 @@ WALK_FWD, WALK_DKDV, WALK_DQ = 0, 1, 2
 CELL = 128
 
 EXPORTS = ("fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd_dkdv_workspace_bytes", "fa_bwd", "fa_bwd_preprocess",
-           "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_splitkv_workspace_bytes",
+           "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_delta", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_splitkv_workspace_bytes",
            "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_fwd_splitkv_fp8kv", "fa_fwd_fp8", "fa_debug_visits", "fa_status_str")
 
 
@@ -57,6 +57,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fa_bwd_preprocess": [P, P, P, I, I, I, I, I, P],
         "fa_bwd_dkdv": [P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, P, S, P],
         "fa_bwd_dq": [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, P],
+        "fa_bwd_dq_delta": [P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, P],
         "fa_fwd_dropout": [P, P, P, P, P, I, I, I, I, F, I, P, P, I, F, U64, P],
         "fa_bwd_dropout": [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, F, U64, P, S, P],
         "fa_fwd_splitkv_workspace_bytes": [I, I, I, I, I, I],
@@ -379,6 +380,22 @@ def fa_bwd_dq(q, k, v, dO, lse, delta, dq=None, *, scale=None, causal=False, blo
     _call("fa_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(dq),
           B, H, N, d, _scale(scale, d), int(bool(causal)), mb, kl, _dtype_code(q), _stream(stream))
     return dq
+
+
+def fa_bwd_dq_delta(q, k, v, o, dO, lse, delta=None, dq=None, *, scale=None, causal=False, block_mask=None,
+                    kv_len=None, stream=None):
+    """dq and delta = rowsum(dO * O) in one stage (fa_bwd_preprocess + fa_bwd_dq
+    for bf16 in one kernel).  Returns (dq, delta)."""
+    import torch
+    B, H, N, d = _shape(q)
+    _check_square(q, [("k", k), ("v", v), ("o", o), ("dO", dO), ("dq", dq)], B, H, N, block_mask, kv_len,
+                  [("lse", lse), ("delta", delta)])
+    dq = _new(q.shape, q.dtype, q) if dq is None else dq
+    delta = _new((B, H, N), torch.float32, q) if delta is None else delta
+    mb, kl = _mask_args(block_mask, kv_len)
+    _call("fa_bwd_dq_delta", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(dq),
+          B, H, N, d, _scale(scale, d), int(bool(causal)), mb, kl, _dtype_code(q), _stream(stream))
+    return dq, delta
 
 
 def fa_debug_visits(which, B, H, N, d, *, causal=False, block_mask=None, kv_len=None, dtype=FA_BF16,

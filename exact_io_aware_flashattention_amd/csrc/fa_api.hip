@@ -224,6 +224,36 @@ int pre_impl(const void* o, const void* dO, float* delta, int B, int H, int N, i
   return hip_status(fa::launch_bwd_pre(a, dtype, d, static_cast<hipStream_t>(stream)));
 }
 
+// dq, with delta = rowsum(dO * O) formed by the dQ kernel itself and stored
+// (bf16); float32 runs the preprocess and then dq.
+int dq_delta_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                  float* delta, void* dq, int B, int H, int N, int d, float scale, int causal,
+                  const uint8_t* block_mask, const int32_t* kv_len, int dtype, const Drop& drop, void* stream) {
+  if (dtype != FA_BF16) {
+    FA_TRY(pre_impl(o, dO, delta, B, H, N, d, dtype, stream));
+    return dq_impl(q, k, v, dO, lse, delta, dq, B, H, N, d, scale, causal, block_mask, kv_len, dtype, drop, stream);
+  }
+  const Shape s{B, H, N, d, dtype};
+  bool empty = false;
+  FA_TRY(check_shape(s, block_mask, &empty));
+  if (empty) return FA_OK;
+  FA_TRY(check_tensors({q, k, v, o, dO, dq}));
+  FA_TRY(check_rowstats({lse, delta}));
+  FA_TRY(check_masks(block_mask, kv_len));
+  FA_TRY(check_scale(scale));
+  fa::AttnArgs a = make_args(s, scale, causal, block_mask, kv_len);
+  set_drop(a, drop);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dO = dO;
+  a.lse = const_cast<float*>(lse);
+  a.delta = delta;
+  a.out0 = dq;
+  return hip_status(fa::launch_bwd_dq(a, dtype, d, false, static_cast<hipStream_t>(stream)));
+}
+
 size_t split_bytes(int N, int d, int dtype, int has_block_mask) {
   if (N <= 0 || !bf16_head_dim(d) || dtype != FA_BF16 || !has_block_mask) return 0;
   return fa::split_ws_bytes(N, d);
@@ -246,10 +276,10 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   const size_t db = delta_bytes(B, H, N);
   if (workspace_bytes < db + split_bytes(N, d, dtype, block_mask != nullptr)) return FA_ERR_WORKSPACE;
   float* delta = static_cast<float*>(workspace);
-  FA_TRY(pre_impl(o, dO, delta, B, H, N, d, dtype, stream));
-  FA_TRY(dkdv_impl(q, k, v, dO, lse, delta, dk, dv, B, H, N, d, scale, causal, block_mask, kv_len, dtype, drop,
-                   static_cast<unsigned char*>(workspace) + db, workspace_bytes - db, stream));
-  return dq_impl(q, k, v, dO, lse, delta, dq, B, H, N, d, scale, causal, block_mask, kv_len, dtype, drop, stream);
+  FA_TRY(dq_delta_impl(q, k, v, o, dO, lse, delta, dq, B, H, N, d, scale, causal, block_mask, kv_len, dtype, drop,
+                       stream));
+  return dkdv_impl(q, k, v, dO, lse, delta, dk, dv, B, H, N, d, scale, causal, block_mask, kv_len, dtype, drop,
+                   static_cast<unsigned char*>(workspace) + db, workspace_bytes - db, stream);
 }
 
 // Key ranges of a split-key forward: nsplit ranges of tps 64-key tiles each.
@@ -408,6 +438,13 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const
               const float* delta, void* dq, int B, int H, int N, int d, float scale, int causal,
               const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* stream) {
   return dq_impl(q, k, v, dO, lse, delta, dq, B, H, N, d, scale, causal, block_mask, kv_len, dtype, Drop{}, stream);
+}
+
+int fa_bwd_dq_delta(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                    float* delta, void* dq, int B, int H, int N, int d, float scale, int causal,
+                    const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* stream) {
+  return dq_delta_impl(q, k, v, o, dO, lse, delta, dq, B, H, N, d, scale, causal, block_mask, kv_len, dtype, Drop{},
+                       stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,

@@ -13,7 +13,7 @@
 // for the products that contract over the tile rows.  Up to d = 128 all three
 // kernels run at least two waves per SIMD (at most 256 registers per wave) so
 // one wave's softmax and mask work overlaps another wave's matrix-core work;
-// dQ at d = 64 runs three.
+// the forward and dQ at d = 64 run three.
 // Head dimensions: multiples of 32 from 64 to 256 (instantiated: 64, 96, 128,
 // 160, 256); a dimension that is not a power of two uses the LDS tile layout
 // of the next power of two (fa_tile.hpp) and the loops run over its D / 16
@@ -795,6 +795,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DqB<D>::OCC,
     if (myq < N) {
       const float l = a.lse[(size_t)bh * N + myq];
       lse2 = (l == neg_inf()) ? pos_inf() : l * LOG2E;
+    }
+    if (a.o) {
+      // delta_i = dO_i . O_i of this lane's row, formed here and stored for
+      // the dK/dV stage: the two lane halves hold alternate 8-element chunks
+      // of the row, as for dO, so each sums its half in fp32 and the halves
+      // are added
+      const bf16* Og = reinterpret_cast<const bf16*>(a.o) + head;
+      float part = 0.f;
+#pragma unroll
+      for (int s = 0; s < C::SSTEPS; ++s) {
+        const u32x4 o4 = myq < N ? ld16(Og + (size_t)myq * D + s * 16 + 8 * h) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          part = __builtin_fmaf(__uint_as_float(o4[w] << 16), __uint_as_float(gf[s][w] << 16), part);
+          part = __builtin_fmaf(__uint_as_float(o4[w] & 0xffff0000u), __uint_as_float(gf[s][w] & 0xffff0000u), part);
+        }
+      }
+      del = sum_halves(part);
+      if (myq < N && h == 0) a.delta[(size_t)bh * N + myq] = del;
+    } else if (myq < N) {
       del = a.delta[(size_t)bh * N + myq];
     }
     f32x16 dq[C::NB];

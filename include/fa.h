@@ -119,8 +119,9 @@ size_t fa_bwd_dkdv_workspace_bytes(int N, int d, int dtype, int has_block_mask);
 
 /*
  * Backward pass for the loss gradient dO: writes dq, dk, dv (dtype).  Runs
- * fa_bwd_preprocess, fa_bwd_dkdv and fa_bwd_dq in that order on `stream`,
- * with delta, then the dk/dv workspace, in `workspace` (at least
+ * fa_bwd_dq_delta and then fa_bwd_dkdv on `stream` (FA_F32: fa_bwd_preprocess,
+ * fa_bwd_dq, fa_bwd_dkdv), with delta, then the dk/dv workspace, in
+ * `workspace` (at least
  * fa_bwd_workspace_bytes bytes for the same sizes and mask presence, 16-byte
  * aligned; its contents need no initialisation and are overwritten).  o and lse must be the outputs of fa_fwd on the same q, k, v,
  * scale and masks.  The pages print no backward equations; the ones used
@@ -163,6 +164,21 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
               const float* lse, const float* delta, void* dq,
               int B, int H, int N, int d, float scale, int causal,
               const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* stream);
+
+/*
+ * Backward stages 1 and 3 in one: dq as fa_bwd_dq, with delta [B,H,N] float32
+ * = rowsum(dO * O) formed by the dQ kernel from o and dO (each row by the
+ * work-group that owns it, fp32 accumulation) and written to `delta` for
+ * fa_bwd_dkdv, which must run after it on the same stream.  The same
+ * quantities as fa_bwd_preprocess followed by fa_bwd_dq (delta may differ in
+ * the last bits: another summation order), without the separate pass over dO
+ * and O.  FA_F32 runs exactly those two calls.  Errors as fa_bwd_dq; o as for
+ * fa_bwd.
+ */
+int fa_bwd_dq_delta(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                    const float* lse, float* delta, void* dq,
+                    int B, int H, int N, int d, float scale, int causal,
+                    const uint8_t* block_mask, const int32_t* kv_len, int dtype, void* stream);
 
 /*
  * Test hook for the tile-skip schedule.  Runs the tile walk of the forward

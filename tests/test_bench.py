@@ -42,15 +42,19 @@ def test_compulsory_bytes():
     t, r = B * H * N * d * 2, B * H * N * 4
     assert bench.kernel_bytes("fwd", B, H, N, d, 2) == 4 * t + r          # Q, K, V in; O, lse out
     assert bench.kernel_bytes("dkdv", B, H, N, d, 2) == 6 * t + 2 * r     # Q, K, V, dO, lse, delta in; dK, dV out
-    assert bench.kernel_bytes("dq", B, H, N, d, 2) == 5 * t + 2 * r
+    assert bench.kernel_bytes("dq", B, H, N, d, 2) == 6 * t + 2 * r       # Q, K, V, dO, O, lse in; dQ, delta out
 
 
 def test_bound_from_arithmetic_intensity():
     w = WORKLOADS[4]
     f = bench.workload_fwd_flops(w, {})
-    table = bench.kernel_table(w, {"fwd": 1.0, "pre": 0.02, "dkdv": 2.0, "dq": 1.5}, f, 1, 16, 16384, 128)
-    assert table["fwd"]["bound"] == "mfma" and table["pre"]["bound"] == "hbm"
+    table = bench.kernel_table(w, {"fwd": 1.0, "dkdv": 2.0, "dq": 1.5}, f, 1, 16, 16384, 128)
+    assert table["fwd"]["bound"] == "mfma" and table["dkdv"]["bound"] == "mfma"
     assert math.isclose(table["fwd"]["tflops"], f / 1e-3 / 1e12, rel_tol=1e-3)
+    # the GPT-2 shape (N = 1024, d = 64, causal): the forward's intensity is below the ridge
+    w2 = WORKLOADS[2]
+    t2 = bench.kernel_table(w2, {"fwd": 0.03}, bench.workload_fwd_flops(w2, {}), w2.B, w2.H, w2.N, w2.d)
+    assert t2["fwd"]["bound"] == "hbm"
 
 
 def test_more_than_one_gpu_is_refused():
@@ -97,8 +101,8 @@ def test_profiled_kernel_names_exist_in_the_library():
 def test_kernel_table_reports_median_min_and_measured_traffic():
     w = WORKLOADS[4]
     f = bench.workload_fwd_flops(w, {})
-    per = {"fwd": 1.0, "pre": 0.02, "dkdv": 2.0, "dq": 1.5}
-    samples = {"fwd": [0.9, 1.0, 1.1], "pre": [0.02] * 3, "dkdv": [2.0, 1.9, 2.1], "dq": [1.5, 1.6, 1.4]}
+    per = {"fwd": 1.0, "dkdv": 2.0, "dq": 1.5}
+    samples = {"fwd": [0.9, 1.0, 1.1], "dkdv": [2.0, 1.9, 2.1], "dq": [1.5, 1.6, 1.4]}
     table = bench.kernel_table(w, per, f, 1, 16, 16384, 128, samples, {"fwd": 8e8})
     assert table["fwd"]["ms_median"] == 1.0 and table["fwd"]["ms_min"] == 0.9
     assert math.isclose(table["fwd"]["hbm_gbs"], 8e8 / 1e-3 / 1e9, rel_tol=1e-3)

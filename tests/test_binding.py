@@ -103,6 +103,12 @@ def test_backward_arguments():
         fa.fa_bwd_dkdv(q, k, v, do, lse, t(B, H, 1, dtype=torch.float32))
     with pytest.raises(TypeError, match="delta must be torch.float32"):
         fa.fa_bwd_dq(q, k, v, do, lse, t(B, H, N))
+    with pytest.raises(ValueError, match="o must have shape"):
+        fa.fa_bwd_dq_delta(q, k, v, t(B, H, N, D // 2), do, lse)
+    with pytest.raises(ValueError, match="delta must have shape"):
+        fa.fa_bwd_dq_delta(q, k, v, o, do, lse, delta=t(B, H, N + 1, dtype=torch.float32))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.fa_bwd_dq_delta(q, k, v, o, do, lse)
 
 
 def test_split_key_arguments():

@@ -5,7 +5,8 @@ and a backward error could mask or mimic each other.  Here the backward gets
 the oracle's O (rounded to the working dtype, as a caller would store it) and
 the oracle's lse, and the dK/dV and dQ stages get delta computed in fp64 from
 the oracle's O, so each stage is compared with the oracle's gradients with
-nothing of the GPU forward in its inputs.  delta_i = dO_i . O_i equals the
+nothing of the GPU forward in its inputs; fa_bwd_dq_delta (dQ forming delta
+itself) gets the oracle's O and lse.  delta_i = dO_i . O_i equals the
 definition sum_j P_ij dP_ij because O_i = sum_j P_ij V_j (bornlex "Flash
 Attention", "Standard Attention", with dP = dO V^T by the chain rule).
 """
@@ -88,4 +89,12 @@ def test_backward_from_oracle_forward(case):
     bound = d * 2.0 ** -24 * np.abs(do_h * o_h).sum(axis=-1) + 1e-30
     err = np.abs(got - want)
     say(f"  delta max err {err.max():.3e} (max bound {bound.max():.3e})")
+    assert np.all(err <= bound)
+
+    # dQ forming delta itself from the oracle's O: the same bound on delta,
+    # and dQ against the oracle's gradient
+    dq3, delta3 = fa.fa_bwd_dq_delta(q, k, v, o, do, tl, **gkw)
+    compare_grad(host(dq3), g_ref[0], dt, "dq_delta dq", zero_scale=zs)
+    err = np.abs(delta3.cpu().numpy().astype(np.float64) - want)
+    say(f"  dq_delta delta max err {err.max():.3e}")
     assert np.all(err <= bound)

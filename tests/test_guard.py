@@ -1,7 +1,7 @@
 """Guard bands around every output: no store lands outside its tensor.
 
-Each output (O, lse, dQ, dK, dV, the split-key O and lse, the FP8 forward's O
-and lse) and the caller-provided workspace is placed inside a larger buffer
+Each output (O, lse, dQ, dK, dV, delta, the split-key O and lse, the FP8
+forward's O and lse) and the caller-provided workspace is placed inside a larger buffer
 whose bytes on both sides hold a sentinel pattern.  After the call the
 sentinels must be unchanged, and the in-bounds results must equal those of
 the same call on ordinary tensors bit for bit (the kernels are
@@ -94,6 +94,14 @@ def test_square_forward_backward_stay_in_bounds(N, d):
     ref = fa.fa_bwd(q, k, v, o_ref, do, lse_ref, **kw)
     for g, r in zip(grads, ref):
         assert same(g.t, r)
+
+    # the dQ stage that also writes delta: both outputs in guard bands; its dQ
+    # is fa_bwd's (the same kernel on the same inputs)
+    gdq, gdelta = Guarded(q.shape, torch.bfloat16), Guarded((B, H, N), torch.float32)
+    fa.fa_bwd_dq_delta(q, k, v, o_ref, do, lse_ref, gdelta.t, gdq.t, **kw)
+    gdq.check("dQ (dq_delta)")
+    gdelta.check("delta (dq_delta)")
+    assert same(gdq.t, ref[0])
 
 
 @pytest.mark.parametrize("d", (64, 128, 256))
