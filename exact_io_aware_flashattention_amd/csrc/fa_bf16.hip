@@ -47,6 +47,15 @@ __device__ __forceinline__ void interleave_mfma_valu() {
     __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
   }
 }
+// The same for a region of NM MFMAs with up to NV VALU instructions after each.
+template <int NM, int NV>
+__device__ __forceinline__ void interleave_mfma_valu_n() {
+#pragma unroll
+  for (int g = 0; g < NM; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);   // VALU
+  }
+}
 
 // Max of the 16 accumulator entries of a lane as a depth-3 tree of v_max3.
 __device__ __forceinline__ float max16(const f32x16& s) {
@@ -201,6 +210,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC
       }
       return max16(s);
     };
+    // The same mask without the max (every entry -inf past the walk).
+    auto mask = [&](f32x16& s, int t) {
+      if (t >= nsub) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = neg_inf();
+        return;
+      }
+      mask_max(s, t);
+    };
     // Refresh the running max only when a score exceeds it by more than 2^TAU.
     // The two lane halves hold different keys of the same query and share
     // thr, so the test needs only the lane's own max; the max over both
@@ -221,6 +239,35 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC
         thr = live ? (m_new + TAU) * inv_c : neg_inf();
       }
     };
+    // Up to d = 128 the max test is replaced by a test of the row sum the
+    // softmax forms anyway (SUMT): a lane's 16 probabilities of a sub-block,
+    // relative to the running max, sum to at most lim = 2^TAU unless one of
+    // its scores exceeds the running max by more than TAU (or several come
+    // close); only then is the max formed, the running max moved and the
+    // probabilities formed again.  An overflowed exponential makes the sum
+    // +inf, which also triggers it; while m_run = -inf, lim = -1 sends every
+    // sub-block through the refresh.  This saves the max tree of every
+    // sub-block (1-3 % of the forward).  Above d = 128 the separate max test
+    // is kept: there the extra probability registers turned the tile loop
+    // into a divergent one.
+    constexpr bool SUMT = D <= 128;
+    constexpr float LIM = 256.f;
+    static_assert(TAU == 8.f, "LIM = 2^TAU");
+    float lim = -1.f;
+    auto move_max = [&](float lane_mx) {
+      const float mx = max_halves(lane_mx);
+      const float m_new = fmaxf(m_run, mx * a.c);
+      const float alpha = (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[nb][r] *= alpha;
+      m_run = m_new;
+      const bool live = m_new != neg_inf();
+      neg_mu = live ? -m_new : 0.f;
+      lim = live ? LIM : -1.f;
+    };
     // P~(t) from S(t) (in place), its row sum into l_run, and O^T += V^T P~^T.
     // (The row sum stays in fp32 VALU adds: v_dot2 on the packed bf16 values
     // would halve the instruction count but does not co-execute with the
@@ -228,15 +275,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC
     // entries alike; dropped entries are then zeroed, and the 1 / (1 - p)
     // factor is applied with the final division by the row sum.
     const DropQuad dquad(drop_xch);
-    auto softmax_pv = [&](f32x16& s, int t) {
+    // probabilities of S(t) into p (may be s itself) and the lane's row sum
+    auto probs = [&](const f32x16& s, f32x16& p) -> float {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, neg_mu));
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, neg_mu));
       float t8[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) t8[i] = s[2 * i] + s[2 * i + 1];
+      for (int i = 0; i < 8; ++i) t8[i] = p[2 * i] + p[2 * i + 1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) t8[i] += t8[i + 4];
-      l_run += (t8[0] + t8[2]) + (t8[1] + t8[3]);
+      return (t8[0] + t8[2]) + (t8[1] + t8[3]);
+    };
+    // dropout on P~(t) in p, then O^T += V^T P~^T
+    auto drop_pv = [&](f32x16& s, int t) {
       if constexpr (DROP) {
         // lane (l & 3) of the quad generates the block of key group (l & 3):
         // keys key0 + 8 (l & 3) + 4 h .. +3 x the quad's four queries
@@ -255,6 +306,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC
       for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) mma(acc[nb], vfrag[nb][mm], pb.p[mm]);
+    };
+    // max test form: P~(t) in place of S(t)
+    auto softmax_pv = [&](f32x16& s, int t) {
+      l_run += probs(s, s);
+      drop_pv(s, t);
+    };
+    // sum test form (SUMT): S(t) is kept for a refresh; the region before the
+    // test holds the scores of the next sub-block (hint_scores)
+    auto softmax_pv_sum = [&](f32x16& s, int t) {
+      f32x16 p;
+      float psum = probs(s, p);
+      interleave_mfma_valu_n<C::SSTEPS, (48 + C::SSTEPS - 1) / C::SSTEPS>();
+      if (wave_any(psum > lim)) {
+        move_max(max16(s));
+        psum = probs(s, p);
+      }
+      l_run += psum;
+      drop_pv(p, t);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -287,6 +356,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC
       using S1 = std::integral_constant<int, 1 - STG>;
       tile_begin(j);
       if (!live) return;
+      if constexpr (SUMT) {
+        read_v(S0(), I0());
+        scores(sb);
+        softmax_pv_sum(sa, 2 * j);
+        read_k(S1(), I0());
+        interleave_mfma_valu_n<C::SSTEPS, 2>();
+        read_v(S0(), I1());
+        scores(sa);
+        softmax_pv_sum(sb, 2 * j + 1);
+        read_k(S1(), I1());
+        interleave_mfma_valu_n<C::SSTEPS, 2>();
+        return;
+      }
       read_v(S0(), I0());
       scores(sb);
       softmax_pv(sa, 2 * j);
@@ -308,6 +390,21 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC
       using S1 = std::integral_constant<int, 1 - STG>;
       tile_begin(j);
       if (!live) return;
+      if constexpr (SUMT) {
+        read_v(S0(), I0());
+        scores(sb);
+        softmax_pv_sum(sa, 2 * j);
+        read_k(S1(), I0());
+        interleave_mfma_valu_n<C::SSTEPS, 2>();
+        mask(sb, 2 * j + 1);
+        read_v(S0(), I1());
+        scores(sa);
+        softmax_pv_sum(sb, 2 * j + 1);
+        read_k(S1(), I1());
+        interleave_mfma_valu_n<C::SSTEPS, 2>();
+        mask(sa, 2 * j + 2);
+        return;
+      }
       // sub-block 2j: S(2j+1) while softmax(2j); then O += P~ V
       read_v(S0(), I0());
       scores(sb);
@@ -334,7 +431,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC
         read_k(I0(), I0());
         scores(sa);
         read_k(I0(), I1());
-        refresh(mask_max(sa, 0));
+        if constexpr (SUMT) {
+          mask(sa, 0);
+          move_max(max16(sa));
+        } else {
+          refresh(mask_max(sa, 0));
+        }
       }
       // steps j and j + 1 are interior iff sub-block 2j + 4 needs no mask
       int j = 0;
