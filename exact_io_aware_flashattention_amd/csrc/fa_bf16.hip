@@ -384,41 +384,57 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(FwdB<D>::OCC
       interleave_mfma_valu();
       refresh(mx2);
     };
+    // Sub-blocks from nlive on hold no key that any query of this wave may
+    // see (past the causal diagonal of the wave's last query, or wholly past
+    // kv_len): their probabilities are exactly zero, so the edge steps skip
+    // their products (the tile loads and barriers go on for the other waves).
+    // Keys only grow along the walk, so they are a suffix of it.  Not in the
+    // split-key instances (built with the skip, the d = 64 one returned wrong
+    // values in the last two accumulator registers of rows that pass from the
+    // interior to the edge steps, though those rows skip nothing; without it
+    // it is exact) nor in the d = 256 dropout one (the branches cost spills).
+    constexpr bool SKIP = (D <= 160 && !SPLITKV) || MODE == K_PLAIN;
+    int nlive = nsub;
+    if constexpr (SKIP) {
+      const int klim = min(kvl, a.causal ? qw0 + 32 + off : kvl);   // first key no query of the wave sees
+      while (nlive > 0 && key0(nlive - 1) >= klim) --nlive;
+    }
     auto tile_step = [&](auto stg, int j) {
       constexpr int STG = decltype(stg)::value;
       using S0 = std::integral_constant<int, STG>;
       using S1 = std::integral_constant<int, 1 - STG>;
       tile_begin(j);
       if (!live) return;
+      const bool l0 = !SKIP || 2 * j < nlive, l1 = !SKIP || 2 * j + 1 < nlive, l2 = !SKIP || 2 * j + 2 < nlive;
       if constexpr (SUMT) {
         read_v(S0(), I0());
-        scores(sb);
-        softmax_pv_sum(sa, 2 * j);
+        if (l1) scores(sb);
+        if (l0) softmax_pv_sum(sa, 2 * j);
         read_k(S1(), I0());
         interleave_mfma_valu_n<C::SSTEPS, 2>();
-        mask(sb, 2 * j + 1);
+        if (l1) mask(sb, 2 * j + 1);
         read_v(S0(), I1());
-        scores(sa);
-        softmax_pv_sum(sb, 2 * j + 1);
+        if (l2) scores(sa);
+        if (l1) softmax_pv_sum(sb, 2 * j + 1);
         read_k(S1(), I1());
         interleave_mfma_valu_n<C::SSTEPS, 2>();
-        mask(sa, 2 * j + 2);
+        if (l2) mask(sa, 2 * j + 2);
         return;
       }
       // sub-block 2j: S(2j+1) while softmax(2j); then O += P~ V
       read_v(S0(), I0());
-      scores(sb);
-      softmax_pv(sa, 2 * j);
+      if (l1) scores(sb);
+      if (l0) softmax_pv(sa, 2 * j);
       read_k(S1(), I0());
       interleave_mfma_valu();
-      refresh(mask_max(sb, 2 * j + 1));
+      if (l1) refresh(mask_max(sb, 2 * j + 1));
       // sub-block 2j+1: S(2j+2) (next tile) while softmax(2j+1)
       read_v(S0(), I1());
-      scores(sa);
-      softmax_pv(sb, 2 * j + 1);
+      if (l2) scores(sa);
+      if (l1) softmax_pv(sb, 2 * j + 1);
       read_k(S1(), I1());
       interleave_mfma_valu();
-      refresh(mask_max(sa, 2 * j + 2));
+      if (l2) refresh(mask_max(sa, 2 * j + 2));
     };
 
     if (nsub > 0) {
@@ -677,6 +693,7 @@ dkdv_bf16_kernel(AttnArgs a) {
       const bool edge = (kw0 + 32 > kvl) || (a.causal && kw0 + 31 > q0);
 #pragma unroll
       for (int qs = 0; qs < C::QS; ++qs) {
+        if (C::QS > 1 && a.causal && q0 + 32 * qs + 31 < kw0) continue;   // every query before every key
         // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys (lane = key)
         f32x16 s, dp;
         zero(s);
@@ -979,8 +996,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DqB<D>::OCC,
       }
       if (a.causal && kb0 > qw0 + 31) return;
       const bool edge = (kb0 + C::BC > kvl) || (a.causal && kb0 + C::BC - 1 > qw0);
+      // the second 32-key half holds no key that a query of this wave sees
+      const bool half1_dead = kb0 + 32 >= kvl || (a.causal && kb0 + 32 > qw0 + 31);
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
+        if (sb == 1 && half1_dead) break;
         // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries (lane = query)
         f32x16 s, dp;
         zero(s);
