@@ -1079,9 +1079,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DqB<D>::OCC,
 
 // ---------------------------------------------------------------- launchers
 
-template <template <int, bool> class KER, int D>
-struct Launch;
-
 #define FA_DEFINE_LAUNCH(NAME, KERNEL)                                                                   \
   template <int D>                                                                                       \
   static hipError_t NAME(const AttnArgs& a, bool walk_only, hipStream_t s) {                            \
