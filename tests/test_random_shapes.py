@@ -1,5 +1,6 @@
 """GPU parity on seeded random shapes: forward and backward of the attention
-kernels, and the split-key forward, against the fp64 oracle.
+kernels (plain and with dropout), the split-key forward and the FP8 forward,
+against the fp64 oracles.
 
 The hand-picked cases elsewhere pin the edges one at a time; these draw the
 whole configuration at once (sizes on and off the 32/64/128 tile edges, every
@@ -15,6 +16,8 @@ from oracle import attention
 from workloads import draw_kv_len, draw_split_qkv
 
 from gpu_cases import compare_forward, host, say, to_dev
+from test_dropout import test_dropout_parity as dropout_parity
+from test_fp8 import test_fp8_parity_within_e4m3_bound as fp8_parity
 from test_parity import check_full, small_inputs
 
 pytestmark = pytest.mark.gpu
@@ -102,3 +105,45 @@ def test_random_split_key(case):
                                                 causal_offset=Nk - Nq)
     compare_forward(host(o).reshape(B * H, Nq, d), lse.cpu().numpy().astype(np.float64).reshape(B * H, Nq),
                     O, L, "bf16", f"random split-key {case}")
+
+
+def draw_dropout_cases(n, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for _ in range(n):
+        d = int(rng.choice([64, 96, 128, 160, 256]))
+        N = int(rng.choice(SPECIAL_N[:-2])) if rng.random() < 0.5 else int(rng.integers(1, 600))
+        u = rng.random()
+        cases.append((int(rng.integers(1, 3)), int(rng.integers(1, 3)), N, d, bool(rng.random() < 0.5),
+                      "rand" if rng.random() < 0.3 else None, "band" if u < 0.25 else None,
+                      int(rng.integers(1, 256))))
+    return cases
+
+
+DROPOUT_CASES = draw_dropout_cases(12, 20261205)
+
+
+@pytest.mark.parametrize("case", DROPOUT_CASES, ids=lambda c: "B{}H{}N{}d{}{}{}{}t{}".format(
+    c[0], c[1], c[2], c[3], "c" if c[4] else "", "k" if c[5] else "", "m" if c[6] else "", c[7]))
+def test_random_dropout(case):
+    dropout_parity(case)
+
+
+def draw_fp8_cases(n, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for _ in range(n):
+        N = int(rng.choice(SPECIAL_N)) if rng.random() < 0.5 else int(rng.integers(1, 1200))
+        cases.append((int(rng.integers(1, 3)), int(rng.integers(1, 3)), N, int(rng.choice([64, 128])),
+                      bool(rng.random() < 0.5), "rand" if rng.random() < 0.3 else None,
+                      "band" if rng.random() < 0.25 else None))
+    return cases
+
+
+FP8_CASES = draw_fp8_cases(10, 20261206)
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: "B{}H{}N{}d{}{}{}{}".format(
+    c[0], c[1], c[2], c[3], "c" if c[4] else "", "k" if c[5] else "", "m" if c[6] else ""))
+def test_random_fp8(case):
+    fp8_parity(case)
