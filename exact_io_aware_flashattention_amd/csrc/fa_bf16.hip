@@ -90,7 +90,8 @@ struct FwdB {
 //         earlier) while the VALU turns S(t) into P~(t) (exp2, row sum, bf16);
 //         V^T(t) fragments are read from LDS;
 //   B(t): O^T += V^T(t) P~^T(t) on the matrix cores while the VALU masks S(t+1)
-//         and takes its row max; K fragments of t+2 are read.
+//         (edge steps only) and, above d = 128, takes its row max; K fragments
+//         of t+2 are read.
 // K and V tiles have separate two-deep LDS rings.  Per 64-key tile j there is
 // one barrier and one DMA issue (K of tile j+2, V of tile j+1), so every tile
 // is requested two sub-block steps before it is read.

@@ -26,6 +26,12 @@ namespace fa {
 constexpr uint32_t PHILOX_M0 = 0xD2511F53u, PHILOX_M1 = 0xCD9E8D57u;
 constexpr uint32_t PHILOX_W0 = 0x9E3779B9u, PHILOX_W1 = 0xBB67AE85u;
 
+// a ^ b ^ c in one instruction (v_bitop3_b32 with the XOR3 truth table
+// 0x96); the compiler otherwise emits two v_xor_b32.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 // Philox4x32 with 10 rounds.  A round maps (c0, c1, c2, c3) to
 // (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key
 // advances by (W0, W1) between rounds.
@@ -38,9 +44,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     const uint64_t p0 = (uint64_t)PHILOX_M0 * c0, p1 = (uint64_t)PHILOX_M1 * c2;
     const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
     const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
-    c0 = hi1 ^ c1 ^ k0;
+    c0 = xor3(hi1, c1, k0);
     c1 = lo1;
-    c2 = hi0 ^ c3 ^ k1;
+    c2 = xor3(hi0, c3, k1);
     c3 = lo0;
     k0 += PHILOX_W0;
     k1 += PHILOX_W1;
