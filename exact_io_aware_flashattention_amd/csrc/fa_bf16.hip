@@ -654,24 +654,31 @@ dkdv_bf16_kernel(AttnArgs a) {
       const unsigned char* Qs = st;
       const unsigned char* dOs = st + C::TILE;
       if constexpr (PLAIN) {
+        // with two 32-query halves (d = 64) both halves' S and dP products
+        // come first, so the vector work of the first half runs under the
+        // products of the second (dK/dV 2-6 % faster at d = 64)
+        f32x16 s[C::QS], dp[C::QS];
 #pragma unroll
         for (int qs = 0; qs < C::QS; ++qs) {
-          f32x16 s, dp;
-          zero(s);
-          zero(dp);
+          zero(s[qs]);
+          zero(dp[qs]);
 #pragma unroll
           for (int k = 0; k < C::SSTEPS; ++k) {
-            mma(s, as_bf16x8(row_chunk<D>(Qs, 32 * qs + l32, 2 * k + h)), as_bf16x8(kf[k]));
-            mma(dp, as_bf16x8(row_chunk<D>(dOs, 32 * qs + l32, 2 * k + h)),
+            mma(s[qs], as_bf16x8(row_chunk<D>(Qs, 32 * qs + l32, 2 * k + h)), as_bf16x8(kf[k]));
+            mma(dp[qs], as_bf16x8(row_chunk<D>(dOs, 32 * qs + l32, 2 * k + h)),
                 as_bf16x8(VREG ? vfr[k] : row_chunk<D>(Vs, wave * 32 + l32, 2 * k + h)));
           }
+        }
+#pragma unroll
+        for (int qs = 0; qs < C::QS; ++qs) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(stats + 32 * qs + 8 * g + 4 * h);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[4 * g + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], a.c, -l4[e]));
+            for (int e = 0; e < 4; ++e)
+              s[qs][4 * g + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qs][4 * g + e], a.c, -l4[e]));
           }
-          const PackedB pb = pack_bf16(s);
+          const PackedB pb = pack_bf16(s[qs]);
 #pragma unroll
           for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
@@ -680,9 +687,9 @@ dkdv_bf16_kernel(AttnArgs a) {
           for (int g = 0; g < 4; ++g) {
             const f32x4 d4 = *reinterpret_cast<const f32x4*>(stats + C::BQ + 32 * qs + 8 * g + 4 * h);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dp[4 * g + e] = s[4 * g + e] * (dp[4 * g + e] - d4[e]);
+            for (int e = 0; e < 4; ++e) dp[qs][4 * g + e] = s[qs][4 * g + e] * (dp[qs][4 * g + e] - d4[e]);
           }
-          const PackedB db = pack_bf16(dp);
+          const PackedB db = pack_bf16(dp[qs]);
 #pragma unroll
           for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
@@ -951,12 +958,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DqB<D>::OCC,
 
     // The trailing tiles of the walk may hold masked entries for some wave
     // (the diagonal cell under a causal mask, the tile that straddles
-    // kv_len).  Below d = 128 the tiles before them run a body with no mask
-    // code, one basic block over both 32-key halves, so that each half's
-    // exponentials and dS work can overlap products of the other half (dQ
-    // 3-5 % faster at d = 64).  At d = 128 every tile takes the masked body,
-    // which measured slightly faster there.
-    constexpr bool PLAIN_LOOP = D < 128;
+    // kv_len).  Up to d = 128 the tiles before them run a body with no mask
+    // code, one basic block over both 32-key halves, software-pipelined
+    // across the halves (dQ 3-5 % faster at d = 64 than one masked loop; the
+    // pipelining 1-2 % at d = 64 and 128, 4 % at d = 96).
+    constexpr bool PLAIN_LOOP = D <= 128;
     int n_plain = PLAIN_LOOP ? walk.ntiles : 0;
     while (n_plain > 0 && (walk.tile_start(n_plain - 1) + C::BC > kvl ||
                            (a.causal && walk.tile_start(n_plain - 1) + C::BC - 1 > q_lo)))
@@ -973,25 +979,38 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DqB<D>::OCC,
       const unsigned char* Vs = Ks + C::TILE;
       if (!wave_has_rows) return;
       if constexpr (PLAIN) {
+        // both halves' S and dP products first, so that the exponentials and
+        // dS of the first half run under the products of the second, and its
+        // dQ products under the second half's vector work
+        f32x16 s[2], dp[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-          f32x16 s, dp;
-          zero(s);
-          zero(dp);
+          zero(s[sb]);
+          zero(dp[sb]);
 #pragma unroll
           for (int k = 0; k < C::SSTEPS; ++k) {
-            mma(s, as_bf16x8(row_chunk<D>(Ks, 32 * sb + l32, 2 * k + h)), as_bf16x8(qf[k]));
-            mma(dp, as_bf16x8(row_chunk<D>(Vs, 32 * sb + l32, 2 * k + h)), as_bf16x8(gf[k]));
+            mma(s[sb], as_bf16x8(row_chunk<D>(Ks, 32 * sb + l32, 2 * k + h)), as_bf16x8(qf[k]));
+            mma(dp[sb], as_bf16x8(row_chunk<D>(Vs, 32 * sb + l32, 2 * k + h)), as_bf16x8(gf[k]));
           }
+        }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c, -lse2));
+        for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - del);
-          const PackedB db = pack_bf16(dp);
+          for (int r = 0; r < 16; ++r) s[sb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], a.c, -lse2));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dp[sb][r] = s[sb][r] * (dp[sb][r] - del);
+          const PackedB db = pack_bf16(dp[sb]);
 #pragma unroll
           for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm) mma(dq[nb], tr_operand<D>(Ks, 32 * sb + 16 * mm, 32 * nb), db.p[mm]);
+        }
+        if constexpr (D == 128) {
+          // the first half's products alone, the second half's under the
+          // first half's vector work, then the first half's dQ products
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::SSTEPS, 0);
+          interleave_mfma_valu_n<2 * C::SSTEPS, 4>();
+          interleave_mfma_valu_n<2 * C::NB, 8>();
         }
         return;
       }
