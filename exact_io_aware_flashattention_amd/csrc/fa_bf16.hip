@@ -598,17 +598,28 @@ dkdv_bf16_kernel(AttnArgs a) {
       zero(dv[nb]);
     }
 
-    float st_l = 0.f, st_d = 0.f;   // this thread's row statistics of the next tile
+    // This thread's row statistics of the next tile, as loaded.  Nothing
+    // may wait for these loads inside the current tile: counted in order, a
+    // wait for them is also a wait for the tile loads issued just before.
+    // So they are converted only at the next tile, and they take their
+    // address from a scalar buffer resource and a loop-invariant lane offset
+    // (a per-tile address register that a later LDS read reuses makes the
+    // compiler wait for the loads first).  Rows past N read 0 and are
+    // treated at the conversion.
+    float st_l = 0.f, st_d = 0.f;
+    int st_q = 0;
     auto issue = [&](int it) {
       unsigned char* st = smem + VRES + (it & 1) * C::STAGE;
       const int q0 = walk.tile_start(it);
       dma.load(Qh, N, q0, st);
       dma.load(dOh, N, q0, st + C::TILE);
       if (tid < C::BQ) {
-        const int q = q0 + tid;
-        const float l = q < N ? lse_g[q] : neg_inf();
-        st_l = (l == neg_inf()) ? pos_inf() : l * LOG2E;   // empty rows and rows past N get P = 0
-        st_d = q < N ? del_g[q] : 0.f;
+        st_q = q0 + tid;
+        const int bytes = (N - q0) * 4;
+        st_l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+            __builtin_amdgcn_make_buffer_rsrc((void*)(lse_g + q0), (short)0, bytes, 0x00020000), tid * 4, 0, 0));
+        st_d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+            __builtin_amdgcn_make_buffer_rsrc((void*)(del_g + q0), (short)0, bytes, 0x00020000), tid * 4, 0, 0));
       }
     };
     if (walk.ntiles > 0) {
@@ -635,12 +646,13 @@ dkdv_bf16_kernel(AttnArgs a) {
     auto tile = [&](int it, auto plain_c, auto stage_c) {
       constexpr bool PLAIN = decltype(plain_c)::value && !DROP;
       constexpr int STG = decltype(stage_c)::value;   // LDS stage, or -1: it & 1
-      wait_loads();
+      wait_loads_all();
       unsigned char* st = smem + VRES + (STG < 0 ? (it & 1) : STG) * C::STAGE;
       float* stats = reinterpret_cast<float*>(st + 2 * C::TILE);
       if (tid < C::BQ) {
-        stats[tid] = st_l;
-        stats[C::BQ + tid] = st_d;
+        // empty rows and rows past N get P = 0
+        stats[tid] = (st_q >= N || st_l == neg_inf()) ? pos_inf() : st_l * LOG2E;
+        stats[C::BQ + tid] = st_q < N ? st_d : 0.f;
       }
       __syncthreads();
       if constexpr (VREG) {
@@ -971,7 +983,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(DqB<D>::OCC,
     auto tile = [&](int it, auto plain_c, auto stage_c) {
       constexpr bool PLAIN = decltype(plain_c)::value && !DROP;
       constexpr int STG = decltype(stage_c)::value;   // LDS stage, or -1: it & 1
-      wait_loads();
+      wait_loads_all();
       __syncthreads();
       if (it + 1 < walk.ntiles) issue(it + 1);
       const int kb0 = walk.tile_start(it);

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(F8<D>::OCC, 
   // per-lane base plus an immediate.
   auto tile_step = [&](int j, auto stg) {
     constexpr int STG = decltype(stg)::value;
-    wait_loads();
+    wait_loads_all();
     __syncthreads();
     if (j + 1 < ntiles) {
       const int nxt = walk.tile_start(j + 1);

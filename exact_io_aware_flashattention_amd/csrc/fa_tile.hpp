@@ -171,6 +171,15 @@ struct TileDma {
 };
 
 __device__ __forceinline__ void wait_loads() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The same wait issued through the builtin, so that the compiler's own wait
+// accounting knows every vector-memory load issued before it (register loads
+// made before a tile loop included) has completed, and adds no wait for them
+// later in the loop, where it would be counted in order behind the tile
+// loads issued since.  (vmcnt 0; expcnt and lgkmcnt at their maxima.)
+__device__ __forceinline__ void wait_loads_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __asm__ volatile("" ::: "memory");
+}
 
 // One 16-byte chunk (8 bf16) of row r.
 template <int D>
